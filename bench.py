@@ -1,0 +1,287 @@
+"""Benchmark of the trellis-coded GEMV hot path on one MI355X.
+
+Default workload: the dense-MLP decode step at batch 1 (gate K2 5120->17408, up K3
+5120->17408, down K3 17408->5120), i.e. three fused trellis_gemv launches per step.
+Metric: code bytes (in*out*K/8 summed over the three matrices) per second.
+
+Weights are rotated over enough distinct device copies (> 1 GiB in total) that the 256 MB
+Infinity Cache cannot serve them between steps; inputs are resident in HBM before timing.
+
+Prints ONE JSON line (rank 0, N = 1).  Extra workloads (small-batch, MoE, prefill) are
+available with --workload for separate measurement lines.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+ROTATE_BYTES = 1 << 30
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _copies(nbytes_per_copy: int) -> int:
+    return max(2, -(-ROTATE_BYTES // max(1, nbytes_per_copy)))
+
+
+class KernelTimer:
+    """Brackets launches with HIP events on the launch stream; sums the durations."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def launch(self, fn):
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.pairs.append((s, e))
+        return out
+
+    def durations_ms(self):
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
+
+def cpu_baseline_dense(wl, budget_s: float = 12.0):
+    """The CPU oracle on a bounded sample: decode + fp64 forward of whole 128-column output
+    blocks of the three matrices, round robin, until the time budget is spent."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    names = ["gate", "up", "down"]
+    t0 = time.perf_counter()
+    nbytes = 0
+    blocks = 0
+    k = 0
+    while time.perf_counter() - t0 < budget_s:
+        name = names[k % 3]
+        lin = wl.layers[name]
+        J = (k // 3) % (lin.out_features // 128)
+        O.forward_linear(lin, wl.xs[name], col_blocks=[J])
+        nbytes += lin.in_features * 128 * lin.K // 8
+        blocks += 1
+        k += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{blocks} whole 128-column output blocks (decode + fp64 forward) of the gate/up/down "
+                      f"matrices, round robin, {nbytes / 1e6:.1f} MB of code in {dt:.1f} s; host "
+                      f"{platform.processor() or platform.machine()}, os.cpu_count()={os.cpu_count()}, "
+                      f"affinity={len(os.sched_getaffinity(0))}, numpy decode single-threaded, "
+                      f"BLAS threads={blas_threads}"}
+
+
+def run_dense(args, torch, tb, synth):
+    wl = synth.dense_mlp(args.seed, batch=1)
+    names = ["gate", "up", "down"]
+    code_bytes = sum(wl.layers[n].code_bytes for n in names)
+    flops = sum(2 * wl.layers[n].in_features * wl.layers[n].out_features for n in names)
+    R = _copies(code_bytes)
+    _log(f"dense MLP: {code_bytes / 1e6:.2f} MB code per step, {R} weight copies")
+    base = {n: tb.TrellisLinear.from_host(wl.layers[n]) for n in names}
+    copies = [base] + [{n: tb.TrellisLinear(base[n].code.clone(), base[n].rin, base[n].rout, base[n].s_in,
+                                            base[n].s_out, base[n].K) for n in names} for _ in range(R - 1)]
+    xs = {n: torch.from_numpy(wl.xs[n]).cuda() for n in names}
+    ys = {n: torch.empty((1, wl.layers[n].out_features), dtype=torch.float16, device="cuda") for n in names}
+
+    def step(i, timer=None):
+        c = copies[i % R]
+        for n in names:
+            if timer is None:
+                tb.trellis_gemv(c[n], xs[n], out=ys[n])
+            else:
+                timer.launch(lambda n=n: tb.trellis_gemv(c[n], xs[n], out=ys[n]))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_s = torch.cuda.Event(enable_timing=True)
+    t_e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_s.record()
+    for i in range(args.steps):
+        step(i)
+    t_e.record()
+    torch.cuda.synchronize()
+    ms_step = t_s.elapsed_time(t_e) / args.steps
+    # per-launch durations of the dominant kernel (separate pass, same stream and rotation)
+    timer = KernelTimer(torch)
+    for i in range(args.steps):
+        step(i, timer)
+    torch.cuda.synchronize()
+    d = timer.durations_ms()
+    launch_ms = float(np.mean(d))
+    per_matrix_us = {n: float(np.mean(d[k::3])) * 1e3 for k, n in enumerate(names)}
+    achieved = (code_bytes / 3) / (launch_ms * 1e-3) / 1e9
+    value = code_bytes / (ms_step * 1e-3) / 1e9
+    out = {
+        "metric": "trellis GEMV code-bytes GB/s (% HBM peak) at batch 1; prefill TFLOP/s",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": "dense MLP decode, batch 1: gate K2 5120x17408 + up K3 5120x17408 + "
+                               "down K3 17408x5120 (three fused trellis_gemv launches per step)",
+                   "global_batch": 1, "code_bytes_per_step": code_bytes, "weight_copies_rotated": R,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
+        "effective_weight_tflops": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "kernel_us": {k: round(v, 2) for k, v in per_matrix_us.items()},
+    }
+    return out, wl
+
+
+def run_prefill(args, torch, tb, synth):
+    wl = synth.prefill(args.seed)
+    lin = wl.layers["w"]
+    L = tb.TrellisLinear.from_host(lin)
+    x = torch.from_numpy(wl.xs["w"]).cuda()
+    y = torch.empty((x.shape[0], lin.out_features), dtype=torch.float16, device="cuda")
+    for _ in range(max(2, args.warmup)):
+        tb.trellis_gemm(L, x, out=y)
+    torch.cuda.synchronize()
+    n = max(5, args.steps // 4)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(n):
+        tb.trellis_gemm(L, x, out=y)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / n
+    flops = 2.0 * x.shape[0] * lin.in_features * lin.out_features
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": "prefill K3 5120x17408, M=2048", "ms": round(ms, 4), "tflops": round(tf, 1),
+            "frac_of_fp16_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+
+
+def run_small_batch(args, torch, tb, synth, B):
+    wl = synth.small_batch(args.seed, batch=B)
+    names = ["qkv", "z", "out"]
+    code_bytes = sum(wl.layers[n].code_bytes for n in names)
+    R = _copies(code_bytes)
+    base = {n: tb.TrellisLinear.from_host(wl.layers[n]) for n in names}
+    copies = [base] + [{n: tb.TrellisLinear(base[n].code.clone(), base[n].rin, base[n].rout, base[n].s_in,
+                                            base[n].s_out, base[n].K) for n in names} for _ in range(R - 1)]
+    xs = {n: torch.from_numpy(wl.xs[n]).cuda() for n in names}
+    ys = {n: torch.empty((B, wl.layers[n].out_features), dtype=torch.float16, device="cuda") for n in names}
+
+    def step(i):
+        for n in names:
+            tb.trellis_gemv(copies[i % R][n], xs[n], out=ys[n])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(args.steps):
+        step(i)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    return {"workload": f"small-batch decode K2 B={B}", "ms_per_step": round(ms, 5),
+            "code_GBps": round(code_bytes / (ms * 1e-3) / 1e9, 1)}
+
+
+def run_moe(args, torch, tb, synth):
+    """Per token: gate+up over the 8 routed experts (16 products, one launch, shared input
+    vectors) and down (8 products, one launch); routes re-drawn every step over 256 experts."""
+    layer = synth.moe_layer(args.seed)
+    E = len(layer.K)
+    dev = lambda l: tb.TrellisLinear.from_host(l)
+    gate = [dev(layer.gate[e]) for e in range(E)]
+    up = [dev(layer.up[e]) for e in range(E)]
+    down = [dev(layer.down[e]) for e in range(E)]
+    t_gu = tb.ExpertTable(gate + up, shared_side=0)
+    t_d = tb.ExpertTable(down, shared_side=1)
+    r_hi = torch.from_numpy(layer.r_hidden_in).cuda()
+    s_hi = torch.from_numpy(layer.s_hidden_in).cuda()
+    r_ho = torch.from_numpy(layer.r_hidden_out).cuda()
+    s_ho = torch.from_numpy(layer.s_hidden_out).cuda()
+    n_tok = args.warmup + args.steps + 64
+    routes = synth.moe_routes(args.seed, n_tok)
+    routes_gu = torch.from_numpy(np.concatenate([routes, routes + E], axis=1).astype(np.int32)).cuda()
+    routes_d = torch.from_numpy(routes).cuda()
+    xt, xd = synth.moe_token_inputs(args.seed)
+    xt = torch.from_numpy(xt[0]).cuda()
+    xd = torch.from_numpy(xd).cuda()
+    y_gu = torch.empty((16, 2048), dtype=torch.float16, device="cuda")
+    y_d = torch.empty((8, 6144), dtype=torch.float16, device="cuda")
+    bytes_tok = [sum(layer.expert_code_bytes(int(e)) for e in r) for r in routes]
+
+    def step(i):
+        tb.trellis_moe_gemv(t_gu, routes_gu[i], xt, False, r_hi, s_hi, 0, out=y_gu)
+        tb.trellis_moe_gemv(t_d, routes_d[i], xd, True, r_ho, s_ho, 1, out=y_d)
+
+    for i in range(64):  # warm-up tokens route across most of the 256 experts
+        step(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(args.steps):
+        step(64 + i)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    nb = float(np.mean(bytes_tok[64:64 + args.steps]))
+    return {"workload": "MoE decode, 8 of 256 GLM-like experts, K in {2,3,4}", "ms_per_token": round(ms, 5),
+            "code_bytes_per_token": nb, "code_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", default="dense", choices=["dense", "small_batch", "moe", "prefill"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the kernels run on one GPU's share; sharding is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from trellis_coded_bit_amd import binding as tb
+    from trellis_coded_bit_amd import synth
+    tb.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.workload == "dense":
+        out, wl = run_dense(args, torch, tb, synth)
+        if not args.no_prefill:
+            out["prefill"] = run_prefill(args, torch, tb, synth)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_dense(wl)
+        print(json.dumps(out), flush=True)
+    elif args.workload == "small_batch":
+        for B in (1, 2, 4, 8):
+            print(json.dumps(run_small_batch(args, torch, tb, synth, B)), flush=True)
+    elif args.workload == "moe":
+        print(json.dumps(run_moe(args, torch, tb, synth)), flush=True)
+    else:
+        print(json.dumps(run_prefill(args, torch, tb, synth)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * trellis.h -- C ABI of libtrellis.so: products against EXL3-style trellis-coded weights
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources cited by page title and section):
+ *   - Storage ("The escha W2 format, recovered and verified", "Tensor mapping"): a layer
+ *     y = x W with W [in, out] is stored as `code` int16 [in/16][out/16][16*K] (one packed
+ *     16x16 tile per (i, j), input-tile index major), `rin` fp16 [in], `rout` fp16 [out]
+ *     and the escha scale vectors `s_in` f32 [in], `s_out` f32 [out].
+ *   - Decode (same page, "Bit layout" and "Codebook: cb=1 (MCG)"): each tile's 256 symbols
+ *     take the circular 16-bit window that ends at the symbol's own K bits of the tile
+ *     bitstream (32-bit words, most significant bit first, each word = two little-endian
+ *     int16 halves); the state maps through v = s * 0xCBAC1FED, (v & 0x8FFF8FFF) ^
+ *     0x3B603B60, value = fp16(lo) + fp16(hi) rounded to fp16; symbol s lands at tile row
+ *     8*((s>>1)&1) + 2*((s>>3)&3) + (s&1), column 8*((s>>2)&1) + (s>>5)
+ *     ("Escha-W2 runs on Metal", tile/permutation paragraph).
+ *   - Forward ("Escha-W2 runs on Metal", reconstruction paragraph): su = rin*s_in,
+ *     sv = rout*s_out, xh = had(x*su), y = had(xh @ W_hat) * sv, where had() applies the
+ *     normalised Sylvester Hadamard H_128/sqrt(128) to each 128-block of the last axis.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise.  fp16 data is passed as
+ *     uint16_t bit patterns.  All arrays are dense, row-major, with no padding.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every call
+ *     only enqueues work on `stream`: it never allocates, frees or synchronises, and keeps
+ *     no pointer after it returns.  Calls are thread-safe; the error string is per thread.
+ *   - Validation happens on the host BEFORE anything is enqueued.  A failed check returns a
+ *     negative trellis_status and sets trellis_last_error(); nothing is launched.  A launch
+ *     failure returns TRELLIS_EHIP with the HIP error text.  No exception crosses the ABI.
+ *   - Workspaces are owned by the caller.  A workspace must be zero-filled before its first
+ *     use; every call leaves its counters at zero again, so one workspace serves any number
+ *     of back-to-back calls on ONE stream.  Calls that overlap in time (several streams)
+ *     need separate workspaces.  trellis_gemm stores activations in its workspace, so a
+ *     buffer used by trellis_gemm must be zero-filled again before a GEMV or MoE call uses it.
+ */
+#ifndef TRELLIS_H_
+#define TRELLIS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TRELLIS_ABI_VERSION 1
+
+typedef enum {
+  TRELLIS_OK = 0,
+  TRELLIS_EINVAL = -1,      /* bad size, K, cb, batch, side flag or NULL required pointer */
+  TRELLIS_EALIGN = -2,      /* a pointer is not aligned as required */
+  TRELLIS_EWORKSPACE = -3,  /* workspace NULL or smaller than trellis_workspace_bytes() */
+  TRELLIS_EUNSUPPORTED = -4,/* valid request this build does not implement */
+  TRELLIS_EHIP = -5         /* a HIP runtime call failed; see trellis_last_error() */
+} trellis_status;
+
+/* One trellis-coded linear layer, y = x W, W [in_features, out_features].
+ * code  : int16 [in/16][out/16][16*K], 16-byte aligned.
+ * rin   : fp16 [in]  (EXL3 suh);  rout: fp16 [out] (EXL3 svh).
+ * s_in  : f32 [in]  or NULL (= all ones);  s_out: f32 [out] or NULL (= all ones).
+ * K in {2,3,4}; cb must be 1 (the MCG codebook); in and out multiples of 128.
+ * ("The escha W2 format, recovered and verified", "Tensor mapping": the config tensor
+ *  [16, bits, cb, 1, in, out] fixes tile 16, K = bits, cb.) */
+typedef struct {
+  const int16_t *code;
+  const uint16_t *rin;
+  const uint16_t *rout;
+  const float *s_in;
+  const float *s_out;
+  int32_t K;
+  int32_t in_features;
+  int32_t out_features;
+  int32_t cb;
+} trellis_linear;
+
+/* Operation ids for trellis_workspace_bytes(). */
+enum { TRELLIS_OP_GEMV = 0, TRELLIS_OP_GEMM = 1, TRELLIS_OP_MOE_GEMV = 2 };
+
+int trellis_abi_version(void);
+
+/* Text of the last error on the calling thread ("" if none).  Valid until the next call. */
+const char *trellis_last_error(void);
+
+/* Decode packed tiles to the codebook-domain matrix, bit-exact.
+ * ("The escha W2 format ...", "Bit layout" and "Codebook"; "Escha-W2 runs on Metal",
+ *  tile/permutation paragraph.)
+ * code   : int16 [in/16][out/16][16*K], 16-byte aligned.
+ * w_hat  : fp16 out [in][out] = W_hat (no Hadamard, no scales), 16-byte aligned.
+ * states : NULL, or uint16 out [in/16][out/16][256]: each symbol's 16-bit trellis state in
+ *          symbol order (for layout checks).
+ * K in {2,3,4}; in, out multiples of 16. */
+int trellis_decode_tiles(const int16_t *code, int K, int in_features, int out_features,
+                         uint16_t *w_hat, uint16_t *states, void *stream);
+
+/* Blockwise Hadamard-128 with a fused per-channel scale.
+ * ("Escha-W2 runs on Metal", reconstruction paragraph: xh = had(x*su), y = had(y_pre)*sv.)
+ * x   : [rows][n], fp32 if x_is_fp32 else fp16.       y: [rows][n], fp32 if y_is_fp32 else fp16.
+ * r   : fp16 [n] or NULL (ones);  s: f32 [n] or NULL (ones).
+ * post = 0: y = had(x * r * s)      (input side)
+ * post = 1: y = had(x) * r * s      (output side)
+ * had() is the normalised H_128/sqrt(128) on each consecutive 128-block; n % 128 == 0,
+ * rows >= 0 (0 is a no-op).  x and y may alias exactly (in place). */
+int had128_scale(const void *x, int x_is_fp32, int rows, int n, const uint16_t *r, const float *s,
+                 int post, void *y, int y_is_fp32, void *stream);
+
+/* Bytes of workspace needed by an op.  op = TRELLIS_OP_GEMV (batch_or_M = B),
+ * TRELLIS_OP_GEMM (batch_or_M = M), TRELLIS_OP_MOE_GEMV (L = any entry of the uniform
+ * table: only in/out are read, batch_or_M ignored, n_routed = n).  Host pointer L.
+ * Returns 0 for invalid arguments. */
+size_t trellis_workspace_bytes(int op, const trellis_linear *L, int batch_or_M, int n_routed);
+
+/* Small-batch product y = had(had(x*su) @ W_hat) * sv.
+ * ("Escha-W2 runs on Metal", reconstruction paragraph.)
+ * L  : HOST pointer to the layer descriptor (its array pointers are device pointers).
+ * x  : fp16 [B][in], y: fp16 out [B][out]; 1 <= B <= 8.
+ * ws : zero-initialised device workspace of >= trellis_workspace_bytes(GEMV, L, B, 0) bytes. */
+int trellis_gemv(const trellis_linear *L, const uint16_t *x, int B, uint16_t *y,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/* Prefill product, same definition as trellis_gemv for M rows (M >= 1).
+ * x: fp16 [M][in], y: fp16 out [M][out].
+ * ws: device workspace of >= trellis_workspace_bytes(GEMM, L, M, 0) bytes (holds the
+ *     rotated activations). */
+int trellis_gemm(const trellis_linear *L, const uint16_t *x, int M, uint16_t *y,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/* Routed-expert products for one token: for k in [0, n), with e = routed[k],
+ *   y[k] = had(had(x_k * su_e) @ W_hat_e) * sv_e,
+ * x_k = x (shared, x_per_expert = 0, fp16 [in]) or x + k*in (x_per_expert = 1, fp16 [n][in]).
+ * ("EXLR8" page: routed experts with per-expert widths K2/K3/K4; a pointer table re-read
+ *  every launch; one hidden-side rotation shared by all experts so the token is rotated
+ *  once.)
+ * experts     : DEVICE array of E descriptors (uniform in_features/out_features, per-entry
+ *               K, per-entry pointers); re-read on every launch.
+ * routed      : DEVICE int32 [n], entries in [0, E).
+ * shared_side : -1 none; 0: the input-side vectors of every entry are replaced by
+ *               (shared_r, shared_s); 1: the output-side vectors are.  shared_r is fp16,
+ *               shared_s is f32 or NULL.
+ * y           : fp16 out [n][out].
+ * An entry that is out of range or has an invalid K produces a zero output row and sets
+ * the error word at the start of the workspace (uint32, non-zero = bad entry seen); check
+ * tables once with trellis_validate_table(). */
+int trellis_moe_gemv(const trellis_linear *experts, int E, const int32_t *routed, int n,
+                     int in_features, int out_features, const uint16_t *x, int x_per_expert,
+                     const uint16_t *shared_r, const float *shared_s, int shared_side,
+                     uint16_t *y, void *ws, size_t ws_bytes, void *stream);
+
+/* Host-side check of a HOST copy of an expert table: K, cb, sizes, alignment, non-NULL
+ * pointers (rin/rout may be NULL on a side that will be shared).  Returns TRELLIS_OK or the
+ * first failing status (with the entry index in trellis_last_error()). */
+int trellis_validate_table(const trellis_linear *host_table, int E, int in_features,
+                           int out_features, int shared_side);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRELLIS_H_ */

@@ -282,17 +282,19 @@ def moe_forward(layer, routed: Iterable[int], x_token: np.ndarray, x_down: np.nd
     expert.  Reading A13: hidden-side scale vectors r_hidden_in/s_hidden_in (gate/up input)
     and r_hidden_out/s_hidden_out (down output) are shared; the 2048-wide side is per expert.
     Reading A14: down's input is per expert.  Reading A15: no router-weighted combine.
-    Returns (gate [n, 2048], up [n, 2048], down [n, 6144]) float64.
+    ``col_blocks`` is None or a pair (blocks of the gate/up outputs, blocks of the down
+    outputs).  Returns (gate [n, 2048], up [n, 2048], down [n, 6144]) float64.
     """
+    cb_gu, cb_d = (None, None) if col_blocks is None else col_blocks
     g, u, d = [], [], []
     for k, e in enumerate(routed):
         ge, ue, de = layer.gate[e], layer.up[e], layer.down[e]
         g.append(forward(ge.code, ge.K, layer.r_hidden_in, ge.rout, layer.s_hidden_in, ge.s_out,
-                         x_token, col_blocks)[0])
+                         x_token, cb_gu)[0])
         u.append(forward(ue.code, ue.K, layer.r_hidden_in, ue.rout, layer.s_hidden_in, ue.s_out,
-                         x_token, col_blocks)[0])
+                         x_token, cb_gu)[0])
         d.append(forward(de.code, de.K, de.rin, layer.r_hidden_out, de.s_in, layer.s_hidden_out,
-                         x_down[k:k + 1], col_blocks)[0])
+                         x_down[k:k + 1], cb_d)[0])
     return np.stack(g), np.stack(u), np.stack(d)
 
 

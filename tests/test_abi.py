@@ -1,0 +1,126 @@
+"""The C-ABI library loads, exports what include/trellis.h declares, and rejects bad
+arguments before launching anything.  No GPU is needed: every call here fails validation
+on the host (pointers are fake, never dereferenced)."""
+import ctypes
+import os
+
+import pytest
+
+from trellis_coded_bit_amd import binding as tb
+
+EINVAL, EALIGN, EWORKSPACE = -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tb.LIB_PATH):
+        from trellis_coded_bit_amd import build
+        build.build(verbose=False)
+    return tb.lib()
+
+
+def lin(**kw):
+    d = dict(code=0x10000, rin=0x20000, rout=0x30000, s_in=0x40000, s_out=0x50000, K=2,
+             in_features=512, out_features=256, cb=1)
+    d.update(kw)
+    return tb.CLinear(d["code"], d["rin"], d["rout"], d["s_in"], d["s_out"], d["K"], d["in_features"],
+                      d["out_features"], d["cb"])
+
+
+def test_exports_every_declared_symbol(L):
+    names = tb.header_functions()
+    assert set(names) >= {"trellis_decode_tiles", "had128_scale", "trellis_gemv", "trellis_gemm",
+                          "trellis_moe_gemv", "trellis_workspace_bytes", "trellis_validate_table",
+                          "trellis_last_error", "trellis_abi_version"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.trellis_abi_version() == 1
+
+
+def test_workspace_bytes(L):
+    c = lin()
+    assert L.trellis_workspace_bytes(0, ctypes.byref(c), 1, 0) > 0
+    assert L.trellis_workspace_bytes(0, ctypes.byref(c), 9, 0) == 0      # B out of range
+    assert L.trellis_workspace_bytes(1, ctypes.byref(c), 2048, 0) >= 2048 * 512 * 2
+    assert L.trellis_workspace_bytes(2, ctypes.byref(c), 1, 8) > 0
+    assert L.trellis_workspace_bytes(7, ctypes.byref(c), 1, 0) == 0
+    bad = lin(in_features=100)
+    assert L.trellis_workspace_bytes(0, ctypes.byref(bad), 1, 0) == 0
+
+
+@pytest.mark.parametrize("kw,B,status", [
+    (dict(K=5), 1, EINVAL), (dict(K=1), 1, EINVAL), (dict(cb=0), 1, EINVAL),
+    (dict(in_features=100), 1, EINVAL), (dict(out_features=0), 1, EINVAL),
+    (dict(code=None), 1, EINVAL), (dict(rin=None), 1, EINVAL),
+    (dict(code=0x10008), 1, EALIGN), (dict(s_in=0x40002), 1, EALIGN),
+    (dict(), 0, EINVAL), (dict(), 9, EINVAL),
+])
+def test_gemv_validation(L, kw, B, status):
+    c = lin(**kw)
+    r = L.trellis_gemv(ctypes.byref(c), 0x60000, B, 0x70000, 0x80000, 1 << 30, None)
+    assert r == status, L.trellis_last_error()
+    assert L.trellis_last_error()
+
+
+def test_gemv_workspace_checks(L):
+    c = lin()
+    need = L.trellis_workspace_bytes(0, ctypes.byref(c), 1, 0)
+    assert L.trellis_gemv(ctypes.byref(c), 0x60000, 1, 0x70000, 0x80000, need - 1, None) == EWORKSPACE
+    assert L.trellis_gemv(ctypes.byref(c), 0x60000, 1, 0x70000, None, need, None) == EWORKSPACE
+    assert L.trellis_gemv(ctypes.byref(c), 0x60000, 1, 0x70000, 0x80010, need, None) == EWORKSPACE
+    assert L.trellis_gemv(ctypes.byref(c), None, 1, 0x70000, 0x80000, need, None) == EINVAL
+
+
+def test_gemm_validation(L):
+    c = lin()
+    need = L.trellis_workspace_bytes(1, ctypes.byref(c), 64, 0)
+    assert L.trellis_gemm(ctypes.byref(c), 0x60000, -1, 0x70000, 0x80000, need, None) == EINVAL
+    assert L.trellis_gemm(ctypes.byref(c), 0x60000, 0, 0x70000, 0x80000, need, None) == 0  # no-op
+    assert L.trellis_gemm(ctypes.byref(c), 0x60008, 64, 0x70000, 0x80000, need, None) == EALIGN
+    assert L.trellis_gemm(ctypes.byref(c), 0x60000, 64, 0x70000, 0x80000, need - 256, None) == EWORKSPACE
+
+
+def test_decode_and_hadamard_validation(L):
+    assert L.trellis_decode_tiles(0x10000, 5, 512, 256, 0x20000, None, None) == EINVAL
+    assert L.trellis_decode_tiles(0x10000, 2, 40, 256, 0x20000, None, None) == EINVAL
+    assert L.trellis_decode_tiles(0x10002, 2, 512, 256, 0x20000, None, None) == EALIGN
+    assert L.trellis_decode_tiles(0x10000, 2, 0, 256, 0x20000, None, None) == 0  # empty
+    assert L.trellis_decode_tiles(None, 2, 512, 256, 0x20000, None, None) == EINVAL
+    assert L.had128_scale(0x10000, 0, 4, 100, None, None, 0, 0x20000, 0, None) == EINVAL
+    assert L.had128_scale(0x10000, 0, 4, 128, None, None, 2, 0x20000, 0, None) == EINVAL
+    assert L.had128_scale(0x10000, 0, 4, 128, None, None, 0, 0x10080, 0, None) == EINVAL  # partial overlap
+    assert L.had128_scale(0x10000, 1, 4, 128, None, None, 0, 0x10000, 0, None) == EINVAL  # in place, mixed types
+    assert L.had128_scale(0x10001, 0, 4, 128, None, None, 0, 0x20000, 0, None) == EALIGN
+    assert L.had128_scale(0x10000, 0, 0, 128, None, None, 0, 0x20000, 0, None) == 0
+
+
+def test_moe_validation_and_table(L):
+    probe = lin(in_features=6144, out_features=2048)
+    need = L.trellis_workspace_bytes(2, ctypes.byref(probe), 1, 8)
+    args = dict(E=4, routed=0x90000, n=8, i=6144, o=2048, x=0x60000, xpe=0, sr=0xA0000, ss=None, side=0,
+                y=0x70000, ws=0x80000, nb=need)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return L.trellis_moe_gemv(0x10000, a["E"], a["routed"], a["n"], a["i"], a["o"], a["x"], a["xpe"],
+                                  a["sr"], a["ss"], a["side"], a["y"], a["ws"], a["nb"], None)
+
+    assert call(side=2) == EINVAL
+    assert call(side=0, sr=None) == EINVAL
+    assert call(E=0) == EINVAL
+    assert call(i=6000) == EINVAL
+    assert call(xpe=2) == EINVAL
+    assert call(nb=need - 1) == EWORKSPACE
+    assert call(n=0) == 0
+    table = (tb.CLinear * 4)(*[lin(in_features=6144, out_features=2048, K=k) for k in (2, 3, 4, 2)])
+    assert L.trellis_validate_table(table, 4, 6144, 2048, -1) == 0
+    table[3].K = 7
+    assert L.trellis_validate_table(table, 4, 6144, 2048, -1) == EINVAL
+    assert b"entry 3" in L.trellis_last_error()
+    table[3].K = 2
+    table[1].rin = None
+    assert L.trellis_validate_table(table, 4, 6144, 2048, -1) == EINVAL
+    assert L.trellis_validate_table(table, 4, 6144, 2048, 0) == 0  # input side shared
+    table[2].out_features = 4096
+    assert L.trellis_validate_table(table, 4, 6144, 2048, 0) == EINVAL

@@ -1,0 +1,274 @@
+"""Thin ctypes binding of libtrellis.so (argument marshalling only).
+
+Every computation runs in the HIP library; this module checks dtypes, devices and
+contiguity, allocates outputs and workspaces with torch, and passes raw device pointers
+and the current HIP stream.  If the library is not built, loading fails loudly: there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtrellis.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "trellis.h")
+
+TRELLIS_OP_GEMV, TRELLIS_OP_GEMM, TRELLIS_OP_MOE_GEMV = 0, 1, 2
+STATUS = {0: "TRELLIS_OK", -1: "TRELLIS_EINVAL", -2: "TRELLIS_EALIGN", -3: "TRELLIS_EWORKSPACE",
+          -4: "TRELLIS_EUNSUPPORTED", -5: "TRELLIS_EHIP"}
+
+
+class TrellisError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class CLinear(ctypes.Structure):
+    """Mirror of ``trellis_linear`` in include/trellis.h."""
+
+    _fields_ = [
+        ("code", ctypes.c_void_p),
+        ("rin", ctypes.c_void_p),
+        ("rout", ctypes.c_void_p),
+        ("s_in", ctypes.c_void_p),
+        ("s_out", ctypes.c_void_p),
+        ("K", ctypes.c_int32),
+        ("in_features", ctypes.c_int32),
+        ("out_features", ctypes.c_int32),
+        ("cb", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtrellis.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is not built; run `python -m trellis_coded_bit_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+            L.trellis_abi_version.restype = i32
+            L.trellis_abi_version.argtypes = []
+            L.trellis_last_error.restype = ctypes.c_char_p
+            L.trellis_last_error.argtypes = []
+            L.trellis_decode_tiles.restype = i32
+            L.trellis_decode_tiles.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+            L.had128_scale.restype = i32
+            L.had128_scale.argtypes = [vp, i32, i32, i32, vp, vp, i32, vp, i32, vp]
+            L.trellis_workspace_bytes.restype = sz
+            L.trellis_workspace_bytes.argtypes = [i32, ctypes.POINTER(CLinear), i32, i32]
+            L.trellis_gemv.restype = i32
+            L.trellis_gemv.argtypes = [ctypes.POINTER(CLinear), vp, i32, vp, vp, sz, vp]
+            L.trellis_gemm.restype = i32
+            L.trellis_gemm.argtypes = [ctypes.POINTER(CLinear), vp, i32, vp, vp, sz, vp]
+            L.trellis_moe_gemv.restype = i32
+            L.trellis_moe_gemv.argtypes = [vp, i32, vp, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, sz, vp]
+            L.trellis_validate_table.restype = i32
+            L.trellis_validate_table.argtypes = [ctypes.POINTER(CLinear), i32, i32, i32, i32]
+            _lib = L
+    return _lib
+
+
+def header_functions() -> List[str]:
+    """Names of the functions include/trellis.h declares."""
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const\s+char\s*\*)\s*\*?\s*(\w+)\s*\(", txt, flags=re.M)
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise TrellisError(status, lib().trellis_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _req(t: torch.Tensor, dtype: torch.dtype, name: str, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------------------
+# Workspaces: zero-filled once, reused by back-to-back calls on one stream.
+# ---------------------------------------------------------------------------------------
+
+_ws: Dict[Tuple[int, int, int], torch.Tensor] = {}
+
+
+def workspace(nbytes: int, device: torch.device, op: int) -> torch.Tensor:
+    """Per (device, stream, op kind): the GEMM workspace holds activations, the GEMV/MoE
+    workspaces hold self-resetting counters, so the kinds never share one."""
+    key = (device.index if device.index is not None else torch.cuda.current_device(), _stream(), op)
+    w = _ws.get(key)
+    if w is None or w.numel() < nbytes:
+        w = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws[key] = w
+    return w
+
+
+class TrellisLinear:
+    """Device tensors of one trellis-coded layer (y = x W, W [in, out])."""
+
+    def __init__(self, code: torch.Tensor, rin: torch.Tensor, rout: torch.Tensor,
+                 s_in: Optional[torch.Tensor], s_out: Optional[torch.Tensor], K: int):
+        self.code, self.rin, self.rout, self.s_in, self.s_out, self.K = code, rin, rout, s_in, s_out, int(K)
+        ti, tj, nw = code.shape
+        self.in_features, self.out_features = 16 * ti, 16 * tj
+        if nw != 16 * self.K:
+            raise ValueError(f"code last dim {nw} != 16*K")
+        dev = code.device
+        _req(code, torch.int16, "code")
+        _req(rin, torch.float16, "rin", dev)
+        _req(rout, torch.float16, "rout", dev)
+        if s_in is not None:
+            _req(s_in, torch.float32, "s_in", dev)
+        if s_out is not None:
+            _req(s_out, torch.float32, "s_out", dev)
+
+    @classmethod
+    def from_host(cls, lin, device="cuda") -> "TrellisLinear":
+        """From a ``synth.Linear`` (numpy arrays)."""
+        t = lambda a: torch.from_numpy(a).to(device)
+        return cls(t(lin.code), t(lin.rin), t(lin.rout), t(lin.s_in), t(lin.s_out), lin.K)
+
+    def c(self) -> CLinear:
+        return CLinear(_ptr(self.code), _ptr(self.rin), _ptr(self.rout), _ptr(self.s_in), _ptr(self.s_out),
+                       self.K, self.in_features, self.out_features, 1)
+
+
+# ---------------------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------------------
+
+def trellis_decode_tiles(code: torch.Tensor, K: int, want_states: bool = False):
+    """code int16 [in/16, out/16, 16K] -> (w_hat fp16 [in, out], states uint16-as-int16 or None)."""
+    _req(code, torch.int16, "code")
+    ti, tj, nw = code.shape
+    if nw != 16 * K:
+        raise ValueError("code last dim must be 16*K")
+    w = torch.empty((16 * ti, 16 * tj), dtype=torch.float16, device=code.device)
+    st = torch.empty((ti, tj, 256), dtype=torch.int16, device=code.device) if want_states else None
+    _check(lib().trellis_decode_tiles(code.data_ptr(), K, 16 * ti, 16 * tj, w.data_ptr(), _ptr(st), _stream()))
+    return w, st
+
+
+def had128_scale(x: torch.Tensor, r: Optional[torch.Tensor] = None, s: Optional[torch.Tensor] = None,
+                 post: bool = False, out_dtype: Optional[torch.dtype] = None,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = had(x*r*s) (post=False) or had(x)*r*s (post=True) over 128-blocks of the last axis."""
+    if x.dtype not in (torch.float16, torch.float32):
+        raise TypeError("x must be float16 or float32")
+    _req(x, x.dtype, "x")
+    n = x.shape[-1]
+    rows = x.numel() // n if n else 0
+    if r is not None:
+        _req(r, torch.float16, "r", x.device)
+    if s is not None:
+        _req(s, torch.float32, "s", x.device)
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    else:
+        _req(out, out.dtype, "out", x.device)
+    _check(lib().had128_scale(x.data_ptr(), int(x.dtype == torch.float32), rows, n, _ptr(r), _ptr(s), int(post),
+                              out.data_ptr(), int(out.dtype == torch.float32), _stream()))
+    return out
+
+
+def trellis_gemv(layer: TrellisLinear, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x fp16 [B, in] (B = 1..8) -> y fp16 [B, out]."""
+    _req(x, torch.float16, "x", layer.code.device)
+    x2 = x.reshape(-1, layer.in_features)
+    B = x2.shape[0]
+    if out is None:
+        out = torch.empty((B, layer.out_features), dtype=torch.float16, device=x.device)
+    L = layer.c()
+    nb = lib().trellis_workspace_bytes(TRELLIS_OP_GEMV, ctypes.byref(L), B, 0)
+    ws = workspace(nb, x.device, TRELLIS_OP_GEMV) if nb else None
+    _check(lib().trellis_gemv(ctypes.byref(L), x2.data_ptr(), B, out.data_ptr(), _ptr(ws), nb, _stream()))
+    return out
+
+
+def trellis_gemm(layer: TrellisLinear, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x fp16 [M, in] -> y fp16 [M, out]."""
+    _req(x, torch.float16, "x", layer.code.device)
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, layer.out_features), dtype=torch.float16, device=x.device)
+    L = layer.c()
+    nb = lib().trellis_workspace_bytes(TRELLIS_OP_GEMM, ctypes.byref(L), M, 0)
+    ws = workspace(nb, x.device, TRELLIS_OP_GEMM)
+    _check(lib().trellis_gemm(ctypes.byref(L), x.data_ptr(), M, out.data_ptr(), _ptr(ws), nb, _stream()))
+    return out
+
+
+class ExpertTable:
+    """A device-resident table of trellis_linear descriptors (uniform in/out, per-entry K)."""
+
+    def __init__(self, layers: Sequence[TrellisLinear], shared_side: int = -1, device="cuda"):
+        self.layers = list(layers)  # keeps the tensors alive
+        self.in_features = self.layers[0].in_features
+        self.out_features = self.layers[0].out_features
+        host = (CLinear * len(self.layers))(*[l.c() for l in self.layers])
+        for i, l in enumerate(self.layers):
+            if shared_side == 0:
+                host[i].rin, host[i].s_in = None, None
+            if shared_side == 1:
+                host[i].rout, host[i].s_out = None, None
+        _check(lib().trellis_validate_table(host, len(self.layers), self.in_features, self.out_features, shared_side))
+        raw = bytes(host)
+        self.table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(device)
+        self.E = len(self.layers)
+
+
+def trellis_moe_gemv(table: ExpertTable, routed: torch.Tensor, x: torch.Tensor, x_per_expert: bool,
+                     shared_r: Optional[torch.Tensor] = None, shared_s: Optional[torch.Tensor] = None,
+                     shared_side: int = -1, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """routed int32 [n] (device); x fp16 [in] or [n, in]; returns y fp16 [n, out]."""
+    _req(routed, torch.int32, "routed")
+    dev = routed.device
+    _req(x, torch.float16, "x", dev)
+    n = routed.numel()
+    if out is None:
+        out = torch.empty((n, table.out_features), dtype=torch.float16, device=dev)
+    probe = CLinear(None, None, None, None, None, 2, table.in_features, table.out_features, 1)
+    nb = lib().trellis_workspace_bytes(TRELLIS_OP_MOE_GEMV, ctypes.byref(probe), 1, n)
+    ws = workspace(nb, dev, TRELLIS_OP_MOE_GEMV)
+    _check(lib().trellis_moe_gemv(table.table.data_ptr(), table.E, routed.data_ptr(), n, table.in_features,
+                                  table.out_features, x.data_ptr(), int(x_per_expert), _ptr(shared_r),
+                                  _ptr(shared_s), shared_side, out.data_ptr(), _ptr(ws), nb, _stream()))
+    return out
+
+
+def moe_error_word(device="cuda") -> int:
+    """The error word of the current stream's workspace (non-zero: a bad table entry was seen)."""
+    key = (torch.device(device).index or 0, _stream(), TRELLIS_OP_MOE_GEMV)
+    w = _ws.get(key)
+    return 0 if w is None else int(w[:4].view(torch.int32).item())

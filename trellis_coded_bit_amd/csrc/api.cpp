@@ -1,0 +1,227 @@
+// C ABI of libtrellis.so: argument validation, error reporting and dispatch to the gfx950
+// launchers.  The contract (meaning, layout, ownership, errors) is in include/trellis.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/trellis.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return TRELLIS_OK;
+  return fail(TRELLIS_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_linear(const trellis_linear *L, int need_side_vectors) {
+  if (!L) return fail(TRELLIS_EINVAL, "layer descriptor is NULL");
+  if (L->K < 2 || L->K > 4) return fail(TRELLIS_EINVAL, "K=%d not in {2,3,4}", L->K);
+  if (L->cb != 1) return fail(TRELLIS_EINVAL, "cb=%d: only the MCG codebook (cb=1) is defined", L->cb);
+  if (L->in_features <= 0 || L->out_features <= 0 || L->in_features % 128 || L->out_features % 128)
+    return fail(TRELLIS_EINVAL, "in=%d out=%d must be positive multiples of 128", L->in_features,
+                L->out_features);
+  if (!L->code) return fail(TRELLIS_EINVAL, "code is NULL");
+  if (!aligned(L->code, 16)) return fail(TRELLIS_EALIGN, "code must be 16-byte aligned");
+  if (need_side_vectors && (!L->rin || !L->rout)) return fail(TRELLIS_EINVAL, "rin/rout is NULL");
+  if ((L->rin && !aligned(L->rin, 2)) || (L->rout && !aligned(L->rout, 2)) ||
+      (L->s_in && !aligned(L->s_in, 4)) || (L->s_out && !aligned(L->s_out, 4)))
+    return fail(TRELLIS_EALIGN, "side vectors must be naturally aligned");
+  return TRELLIS_OK;
+}
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int trellis_abi_version(void) { return TRELLIS_ABI_VERSION; }
+
+const char *trellis_last_error(void) { return g_err; }
+
+int trellis_decode_tiles(const int16_t *code, int K, int in_features, int out_features,
+                         uint16_t *w_hat, uint16_t *states, void *stream) {
+  g_err[0] = 0;
+  if (K < 2 || K > 4) return fail(TRELLIS_EINVAL, "K=%d not in {2,3,4}", K);
+  if (in_features < 0 || out_features < 0 || in_features % 16 || out_features % 16)
+    return fail(TRELLIS_EINVAL, "in=%d out=%d must be non-negative multiples of 16", in_features,
+                out_features);
+  if ((long long)in_features * out_features == 0) return TRELLIS_OK;
+  if (!code || !w_hat) return fail(TRELLIS_EINVAL, "code or w_hat is NULL");
+  if (!aligned(code, 16) || !aligned(w_hat, 16) || (states && !aligned(states, 16)))
+    return fail(TRELLIS_EALIGN, "code, w_hat and states must be 16-byte aligned");
+  return hip_status(trellis::launch_decode_tiles(code, K, in_features, out_features, w_hat, states,
+                                                 as_stream(stream)),
+                    "trellis_decode_tiles launch");
+}
+
+int had128_scale(const void *x, int x_is_fp32, int rows, int n, const uint16_t *r, const float *s,
+                 int post, void *y, int y_is_fp32, void *stream) {
+  g_err[0] = 0;
+  if (rows < 0 || n <= 0 || n % 128) return fail(TRELLIS_EINVAL, "rows=%d n=%d: need rows >= 0, n a positive multiple of 128", rows, n);
+  if (post != 0 && post != 1) return fail(TRELLIS_EINVAL, "post=%d must be 0 or 1", post);
+  if ((long long)rows * (n / 128) > (1LL << 33)) return fail(TRELLIS_EINVAL, "too many rows");
+  if (rows == 0) return TRELLIS_OK;
+  if (!x || !y) return fail(TRELLIS_EINVAL, "x or y is NULL");
+  if (!aligned(x, x_is_fp32 ? 4 : 2) || !aligned(y, y_is_fp32 ? 4 : 2) ||
+      (r && !aligned(r, 2)) || (s && !aligned(s, 4)))
+    return fail(TRELLIS_EALIGN, "arrays must be naturally aligned");
+  if (x != y) {
+    // partial overlap is not supported (exact aliasing is)
+    const char *xa = static_cast<const char *>(x), *ya = static_cast<const char *>(y);
+    const size_t xb = (size_t)rows * n * (x_is_fp32 ? 4 : 2), yb = (size_t)rows * n * (y_is_fp32 ? 4 : 2);
+    if (xa < ya + yb && ya < xa + xb) return fail(TRELLIS_EINVAL, "x and y overlap without being identical");
+  } else if (x_is_fp32 != y_is_fp32) {
+    return fail(TRELLIS_EINVAL, "in-place use needs x and y of the same type");
+  }
+  const float norm = 0.08838834764831845f;  // 1/sqrt(128)
+  return hip_status(trellis::launch_had128(x, x_is_fp32, rows, n, r, s, post, norm, y, y_is_fp32,
+                                           as_stream(stream)),
+                    "had128_scale launch");
+}
+
+size_t trellis_workspace_bytes(int op, const trellis_linear *L, int batch_or_M, int n_routed) {
+  if (!L || L->in_features <= 0 || L->out_features <= 0 || L->in_features % 128 ||
+      L->out_features % 128)
+    return 0;
+  switch (op) {
+    case TRELLIS_OP_GEMV:
+      if (batch_or_M < 1 || batch_or_M > 8) return 0;
+      return trellis::gemv_workspace_bytes(1, L->in_features, L->out_features, batch_or_M);
+    case TRELLIS_OP_GEMM:
+      if (batch_or_M < 0) return 0;
+      return trellis::gemm_workspace_bytes(L->in_features, L->out_features, batch_or_M);
+    case TRELLIS_OP_MOE_GEMV:
+      if (n_routed < 0) return 0;
+      return trellis::gemv_workspace_bytes(n_routed, L->in_features, L->out_features, 1);
+    default:
+      return 0;
+  }
+}
+
+int trellis_gemv(const trellis_linear *L, const uint16_t *x, int B, uint16_t *y, void *ws,
+                 size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  int st = check_linear(L, 1);
+  if (st) return st;
+  if (B < 1 || B > 8) return fail(TRELLIS_EINVAL, "B=%d not in 1..8", B);
+  if (!x || !y) return fail(TRELLIS_EINVAL, "x or y is NULL");
+  if (!aligned(x, 2) || !aligned(y, 2)) return fail(TRELLIS_EALIGN, "x/y must be 2-byte aligned");
+  if (L->out_features / 128 > trellis::gemv_max_column_blocks())
+    return fail(TRELLIS_EINVAL, "out=%d exceeds %d column blocks", L->out_features, trellis::gemv_max_column_blocks());
+  const size_t need = trellis::gemv_workspace_bytes(1, L->in_features, L->out_features, B);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(TRELLIS_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+  trellis::GemvLaunch a{};
+  a.single = *L;
+  a.table = nullptr;
+  a.E = 0;
+  a.routed = nullptr;
+  a.n_problems = 1;
+  a.in_features = L->in_features;
+  a.out_features = L->out_features;
+  a.B = B;
+  a.x = x;
+  a.x_per_problem = 0;
+  a.y = y;
+  a.shared_r = nullptr;
+  a.shared_s = nullptr;
+  a.shared_side = -1;
+  return hip_status(trellis::launch_gemv(a, ws, ws_bytes, as_stream(stream)), "trellis_gemv launch");
+}
+
+int trellis_gemm(const trellis_linear *L, const uint16_t *x, int M, uint16_t *y, void *ws,
+                 size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  int st = check_linear(L, 1);
+  if (st) return st;
+  if (M < 0) return fail(TRELLIS_EINVAL, "M=%d < 0", M);
+  if (M == 0) return TRELLIS_OK;
+  if ((long long)M > (1LL << 24)) return fail(TRELLIS_EINVAL, "M=%d too large", M);
+  if (!x || !y) return fail(TRELLIS_EINVAL, "x or y is NULL");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(TRELLIS_EALIGN, "x/y must be 16-byte aligned");
+  const size_t need = trellis::gemm_workspace_bytes(L->in_features, L->out_features, M);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(TRELLIS_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+  return hip_status(trellis::launch_gemm(*L, x, M, y, ws, ws_bytes, as_stream(stream)),
+                    "trellis_gemm launch");
+}
+
+int trellis_moe_gemv(const trellis_linear *experts, int E, const int32_t *routed, int n,
+                     int in_features, int out_features, const uint16_t *x, int x_per_expert,
+                     const uint16_t *shared_r, const float *shared_s, int shared_side,
+                     uint16_t *y, void *ws, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  if (E <= 0 || !experts) return fail(TRELLIS_EINVAL, "empty or NULL expert table");
+  if (n < 0) return fail(TRELLIS_EINVAL, "n=%d < 0", n);
+  if (in_features <= 0 || out_features <= 0 || in_features % 128 || out_features % 128)
+    return fail(TRELLIS_EINVAL, "in=%d out=%d must be positive multiples of 128", in_features, out_features);
+  if (shared_side < -1 || shared_side > 1) return fail(TRELLIS_EINVAL, "shared_side=%d", shared_side);
+  if (shared_side >= 0 && !shared_r) return fail(TRELLIS_EINVAL, "shared_r is NULL");
+  if (x_per_expert != 0 && x_per_expert != 1) return fail(TRELLIS_EINVAL, "x_per_expert must be 0 or 1");
+  if (n == 0) return TRELLIS_OK;
+  if ((long long)n * (out_features / 128) > trellis::gemv_max_column_blocks())
+    return fail(TRELLIS_EINVAL, "n*out/128 exceeds %d column blocks", trellis::gemv_max_column_blocks());
+  if (!routed || !x || !y) return fail(TRELLIS_EINVAL, "routed, x or y is NULL");
+  if (!aligned(experts, 8) || !aligned(routed, 4) || !aligned(x, 2) || !aligned(y, 2))
+    return fail(TRELLIS_EALIGN, "misaligned table, routed, x or y");
+  const size_t need = trellis::gemv_workspace_bytes(n, in_features, out_features, 1);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(TRELLIS_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+  trellis::GemvLaunch a{};
+  memset(&a.single, 0, sizeof(a.single));
+  a.table = experts;
+  a.E = E;
+  a.routed = routed;
+  a.n_problems = n;
+  a.in_features = in_features;
+  a.out_features = out_features;
+  a.B = 1;
+  a.x = x;
+  a.x_per_problem = x_per_expert;
+  a.y = y;
+  a.shared_r = shared_r;
+  a.shared_s = shared_s;
+  a.shared_side = shared_side;
+  return hip_status(trellis::launch_gemv(a, ws, ws_bytes, as_stream(stream)), "trellis_moe_gemv launch");
+}
+
+int trellis_validate_table(const trellis_linear *host_table, int E, int in_features,
+                           int out_features, int shared_side) {
+  g_err[0] = 0;
+  if (!host_table || E <= 0) return fail(TRELLIS_EINVAL, "empty or NULL table");
+  for (int e = 0; e < E; ++e) {
+    const trellis_linear &L = host_table[e];
+    trellis_linear c = L;
+    if (shared_side == 0 && !c.rin) c.rin = reinterpret_cast<const uint16_t *>(&L);  // shared: may be NULL
+    if (shared_side == 1 && !c.rout) c.rout = reinterpret_cast<const uint16_t *>(&L);
+    int st = check_linear(&c, 1);
+    if (st) {
+      char tmp[512];
+      snprintf(tmp, sizeof(tmp), "entry %d: %s", e, g_err);
+      snprintf(g_err, sizeof(g_err), "%s", tmp);
+      return st;
+    }
+    if (L.in_features != in_features || L.out_features != out_features)
+      return fail(TRELLIS_EINVAL, "entry %d: shape %dx%d differs from %dx%d", e, L.in_features,
+                  L.out_features, in_features, out_features);
+  }
+  return TRELLIS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Device-side building blocks shared by the gfx950 kernels of libtrellis.
+//
+// Method sources (page title, section):
+//   * "The escha W2 format, recovered and verified": "Bit layout" (tile words read as
+//     32-bit words, MSB-first windows ending at each symbol's own K bits, circular) and
+//     "Codebook: cb=1 (MCG), verified" (multiply, mask/xor, sum of two fp16 halves).
+//   * "Escha-W2 runs on Metal": tile/permutation paragraph (symbol -> tile row/column).
+//
+// Lane <-> symbol assignment used by every kernel.  Lane l of a wave (n = l & 15,
+// g = l >> 4) owns the four consecutive symbols s0 + {0,1,2,3} of a tile with
+//     s0 = 32*(n & 7) + 8*g + 4*(n >> 3).
+// By the tile permutation these four symbols all lie in tile column n and in tile rows
+// {2g, 2g+1, 2g+8, 2g+9}.  Their four 16-bit windows span 16 + 3K <= 28 consecutive
+// stream bits, so one 32-bit funnel shift of two tile words holds all of them.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace trellis {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// The MCG hash ("Codebook: cb=1"): v = s * 0xCBAC1FED mod 2^32, then (v & 0x8FFF8FFF) ^
+// 0x3B603B60.  The result, read as two fp16 halves, sums to the codebook value.
+__device__ __forceinline__ uint32_t mcg_hash(uint32_t state) {
+  uint32_t v = state * 0xCBAC1FEDu;
+  return (v & 0x8FFF8FFFu) ^ 0x3B603B60u;
+}
+
+// fp16 codebook value: one binary16 round-to-nearest-even of lo + hi.
+__device__ __forceinline__ _Float16 mcg_value(uint32_t h) {
+  _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(h & 0xFFFFu));
+  _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(h >> 16));
+  return lo + hi;
+}
+
+// Per-lane window geometry inside a tile of K-bit symbols (8K 32-bit words).
+// The lane's four windows start at stream bit `start` = K*s0 + K - 16 (mod 256K).
+// Writing start = 32*d0 + off with off in [1, 32], the 32 stream bits beginning at `start`
+// are alignbit(word[d0], word[d1], 32 - off) with d1 = d0 + 1 (mod 8K); window j is then
+// bits [16 - j*K, 32 - j*K) of that register.
+struct LaneWindow {
+  uint32_t d0, d1, sh;
+};
+
+__device__ __forceinline__ LaneWindow lane_window(int lane, int K) {
+  const int n = lane & 15, g = lane >> 4;
+  const int s0 = 32 * (n & 7) + 8 * g + 4 * (n >> 3);
+  const int nbits = 256 * K, nwords = 8 * K;
+  int start = K * s0 + K - 16;
+  if (start <= 0) start += nbits;  // start in [1, nbits]
+  const int d0 = (start - 1) >> 5;
+  const int off = start - 32 * d0;  // [1, 32]
+  LaneWindow w;
+  w.d0 = (uint32_t)d0;
+  w.d1 = (uint32_t)((d0 + 1) % nwords);
+  w.sh = (uint32_t)(32 - off);
+  return w;
+}
+
+// 32 stream bits starting at the lane's first window.
+__device__ __forceinline__ uint32_t lane_bits(uint32_t w0, uint32_t w1, uint32_t sh) {
+  return __builtin_amdgcn_alignbit(w0, w1, sh);
+}
+
+// State of the lane's symbol s0 + j.
+template <int K>
+__device__ __forceinline__ uint32_t lane_state(uint32_t bits, int j) {
+  return (bits >> (16 - j * K)) & 0xFFFFu;
+}
+
+// Tile row of the lane's symbol s0 + j (j = 0..3): 2g, 2g+1, 2g+8, 2g+9.
+__device__ __forceinline__ int lane_row(int lane, int j) {
+  return 2 * (lane >> 4) + (j & 1) + 8 * (j >> 1);
+}
+
+// Loads through the global address space (the pointers reach the kernels inside structs,
+// so the compiler cannot infer the address space and would otherwise emit flat loads).
+template <typename T>
+__device__ __forceinline__ T ldg(const T *p) {
+  return *(const __attribute__((address_space(1))) T *)p;
+}
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ uint16_t f2h(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Unnormalised Sylvester Hadamard butterfly over 128 values held as two per lane
+// (a = element lane, b = element lane + 64) across a full wave of 64 lanes.
+// Produces (H_128 z)[lane] in a and (H_128 z)[lane + 64] in b.
+__device__ __forceinline__ void wave_fwht128(float &a, float &b) {
+  const int lane = threadIdx.x & 63;
+  float s = a + b, d = a - b;
+  a = s;
+  b = d;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    float pa = __shfl_xor(a, m, 64);
+    float pb = __shfl_xor(b, m, 64);
+    const bool up = (lane & m) != 0;
+    a = up ? (pa - a) : (a + pa);
+    b = up ? (pb - b) : (b + pb);
+  }
+}
+
+}  // namespace trellis
