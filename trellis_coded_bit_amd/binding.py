@@ -152,6 +152,8 @@ class TrellisLinear:
             _req(s_in, torch.float32, "s_in", dev)
         if s_out is not None:
             _req(s_out, torch.float32, "s_out", dev)
+        self._c = None
+        self._ws_bytes = {}
 
     @classmethod
     def from_host(cls, lin, device="cuda") -> "TrellisLinear":
@@ -160,8 +162,18 @@ class TrellisLinear:
         return cls(t(lin.code), t(lin.rin), t(lin.rout), t(lin.s_in), t(lin.s_out), lin.K)
 
     def c(self) -> CLinear:
-        return CLinear(_ptr(self.code), _ptr(self.rin), _ptr(self.rout), _ptr(self.s_in), _ptr(self.s_out),
-                       self.K, self.in_features, self.out_features, 1)
+        if self._c is None:
+            self._c = CLinear(_ptr(self.code), _ptr(self.rin), _ptr(self.rout), _ptr(self.s_in), _ptr(self.s_out),
+                              self.K, self.in_features, self.out_features, 1)
+        return self._c
+
+    def workspace_bytes(self, op: int, batch_or_M: int) -> int:
+        key = (op, batch_or_M)
+        nb = self._ws_bytes.get(key)
+        if nb is None:
+            nb = lib().trellis_workspace_bytes(op, ctypes.byref(self.c()), batch_or_M, 0)
+            self._ws_bytes[key] = nb
+        return nb
 
 
 # ---------------------------------------------------------------------------------------
@@ -202,30 +214,39 @@ def had128_scale(x: torch.Tensor, r: Optional[torch.Tensor] = None, s: Optional[
     return out
 
 
-def trellis_gemv(layer: TrellisLinear, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """x fp16 [B, in] (B = 1..8) -> y fp16 [B, out]."""
+def trellis_gemv(layer: TrellisLinear, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x fp16 [B, in] (B = 1..8) -> y fp16 [B, out].  ``ws``: optional uint8 workspace tensor
+    (at least ``layer.workspace_bytes(TRELLIS_OP_GEMV, B)`` bytes), e.g. for graph capture."""
     _req(x, torch.float16, "x", layer.code.device)
     x2 = x.reshape(-1, layer.in_features)
     B = x2.shape[0]
     if out is None:
         out = torch.empty((B, layer.out_features), dtype=torch.float16, device=x.device)
-    L = layer.c()
-    nb = lib().trellis_workspace_bytes(TRELLIS_OP_GEMV, ctypes.byref(L), B, 0)
-    ws = workspace(nb, x.device, TRELLIS_OP_GEMV) if nb else None
-    _check(lib().trellis_gemv(ctypes.byref(L), x2.data_ptr(), B, out.data_ptr(), _ptr(ws), nb, _stream()))
+    nb = layer.workspace_bytes(TRELLIS_OP_GEMV, B)
+    if ws is None:
+        ws = workspace(nb, x.device, TRELLIS_OP_GEMV)
+    elif ws.numel() < nb:
+        raise ValueError(f"workspace of {ws.numel()} bytes < {nb}")
+    _check(lib().trellis_gemv(ctypes.byref(layer.c()), x2.data_ptr(), B, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                              _stream()))
     return out
 
 
-def trellis_gemm(layer: TrellisLinear, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+def trellis_gemm(layer: TrellisLinear, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """x fp16 [M, in] -> y fp16 [M, out]."""
     _req(x, torch.float16, "x", layer.code.device)
     M = x.shape[0]
     if out is None:
         out = torch.empty((M, layer.out_features), dtype=torch.float16, device=x.device)
-    L = layer.c()
-    nb = lib().trellis_workspace_bytes(TRELLIS_OP_GEMM, ctypes.byref(L), M, 0)
-    ws = workspace(nb, x.device, TRELLIS_OP_GEMM)
-    _check(lib().trellis_gemm(ctypes.byref(L), x.data_ptr(), M, out.data_ptr(), _ptr(ws), nb, _stream()))
+    nb = layer.workspace_bytes(TRELLIS_OP_GEMM, M)
+    if ws is None:
+        ws = workspace(nb, x.device, TRELLIS_OP_GEMM)
+    elif ws.numel() < nb:
+        raise ValueError(f"workspace of {ws.numel()} bytes < {nb}")
+    _check(lib().trellis_gemm(ctypes.byref(layer.c()), x.data_ptr(), M, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                              _stream()))
     return out
 
 
@@ -246,11 +267,21 @@ class ExpertTable:
         raw = bytes(host)
         self.table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(device)
         self.E = len(self.layers)
+        self._ws_bytes = {}
+
+    def workspace_bytes(self, n: int) -> int:
+        nb = self._ws_bytes.get(n)
+        if nb is None:
+            probe = CLinear(None, None, None, None, None, 2, self.in_features, self.out_features, 1)
+            nb = lib().trellis_workspace_bytes(TRELLIS_OP_MOE_GEMV, ctypes.byref(probe), 1, n)
+            self._ws_bytes[n] = nb
+        return nb
 
 
 def trellis_moe_gemv(table: ExpertTable, routed: torch.Tensor, x: torch.Tensor, x_per_expert: bool,
                      shared_r: Optional[torch.Tensor] = None, shared_s: Optional[torch.Tensor] = None,
-                     shared_side: int = -1, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     shared_side: int = -1, out: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """routed int32 [n] (device); x fp16 [in] or [n, in]; returns y fp16 [n, out]."""
     _req(routed, torch.int32, "routed")
     dev = routed.device
@@ -258,12 +289,14 @@ def trellis_moe_gemv(table: ExpertTable, routed: torch.Tensor, x: torch.Tensor, 
     n = routed.numel()
     if out is None:
         out = torch.empty((n, table.out_features), dtype=torch.float16, device=dev)
-    probe = CLinear(None, None, None, None, None, 2, table.in_features, table.out_features, 1)
-    nb = lib().trellis_workspace_bytes(TRELLIS_OP_MOE_GEMV, ctypes.byref(probe), 1, n)
-    ws = workspace(nb, dev, TRELLIS_OP_MOE_GEMV)
+    nb = table.workspace_bytes(n)
+    if ws is None:
+        ws = workspace(nb, dev, TRELLIS_OP_MOE_GEMV)
+    elif ws.numel() < nb:
+        raise ValueError(f"workspace of {ws.numel()} bytes < {nb}")
     _check(lib().trellis_moe_gemv(table.table.data_ptr(), table.E, routed.data_ptr(), n, table.in_features,
                                   table.out_features, x.data_ptr(), int(x_per_expert), _ptr(shared_r),
-                                  _ptr(shared_s), shared_side, out.data_ptr(), _ptr(ws), nb, _stream()))
+                                  _ptr(shared_s), shared_side, out.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
     return out
 
 

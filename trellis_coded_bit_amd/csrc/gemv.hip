@@ -5,32 +5,33 @@
 // pointer table -- "EXLR8" page: per-expert widths, a pointer table re-read every launch,
 // one hidden-side rotation shared by all experts).
 //
-// Work decomposition (stream-K over "units").  A unit is one 128-row input block I times
-// one 128-column output block J of one problem p, i.e. 8x8 tiles; units are numbered
-// u = (p*nJ + J)*nI + I and the G workgroups take equal contiguous ranges of u, so every
-// workgroup streams the same number of code bytes whatever the matrix shape.  A range that
-// cuts a column block leaves a partial sum in the workspace; the last workgroup to finish
-// a column block (agent-scope counter) adds the partials in a fixed order, applies the
-// output Hadamard and the scales, writes fp16 y and resets the counter.  Partial sums are
-// written and read with agent-scope atomic accesses, which are coherent across the XCDs'
-// L2 caches without the full L2 write-back a device-wide fence would cost.
+// Two launches.
 //
-// Inside a workgroup (4 waves) every wave takes two of the unit's eight tile rows:
-//   * loads: the wave's 2 x 8 tiles are 2 x 256K contiguous bytes; each lane loads 8-byte
-//     pieces (fully coalesced) several units ahead of use (a ring of kPrefetch units in
-//     registers keeps a few KB per wave in flight) and stages them in a wave-private LDS
-//     buffer; each tile is stored with a copy of its last word in front, so every lane's
-//     circular window is two adjacent LDS words;
-//   * input rotation: for each group of kSuper units the workgroup butterflies x*su
-//     (unnormalised) and stores fp16 MFMA A-operands in LDS, each value twice (below);
-//   * contraction: per tile each lane decodes its four symbols (trellis_device.h) to four
-//     MCG hash words and feeds them UNSUMMED to v_mfma_f32_16x16x32_f16 as eight fp16
-//     B-elements along k.  The A operand repeats each activation for the lo and hi halves,
-//     so the matrix core forms x*lo + x*hi in fp32 and the codebook's lo+hi addition costs
-//     no VALU work.  One MFMA covers one tile; batch rows ride in the 16 M rows.  (This
-//     fp32 sum of the halves is the exact value before the format's fp16 rounding; it
-//     differs from the rounded codebook value by at most half an fp16 ulp.)
-//   * the two 1/sqrt(128) factors are folded into one exact 1/128 at the output.
+// 1. gemv_partial_kernel (stream-K over "units").  A unit is one 128-row input block I
+//    times one 128-column output block J of one problem p, i.e. 8x8 tiles; units are
+//    numbered u = (p*nJ + J)*nI + I and the G workgroups take equal contiguous ranges of u,
+//    so every workgroup streams the same number of code bytes whatever the matrix shape.
+//    Each workgroup writes one fp32 partial sum y_pre[B][128] per column block it touches
+//    (its "segment") into the workspace.  Inside a workgroup (4 waves) every wave takes
+//    two of the unit's eight tile rows:
+//      * loads: the wave's 2 x 8 tiles are 2 x 256K contiguous bytes; each lane loads
+//        8-byte pieces (fully coalesced) kPrefetch units ahead of use, into a ring of
+//        registers, and stages them in a wave-private LDS buffer; each tile is stored with
+//        a copy of its last word in front, so a lane's circular window is two adjacent
+//        LDS words;
+//      * input rotation: per sub-range the workgroup butterflies x*su (unnormalised) and
+//        stores fp16 MFMA A-operands in LDS, each value twice (below);
+//      * contraction: per tile each lane decodes its four symbols (trellis_device.h) to
+//        four MCG hash words and feeds them UNSUMMED to v_mfma_f32_16x16x32_f16 as eight
+//        fp16 B-elements along k.  The A operand repeats each activation for the lo and hi
+//        halves, so the matrix core forms x*lo + x*hi in fp32 and the codebook's lo+hi
+//        addition costs no VALU work.  One MFMA covers one tile; batch rows ride in the
+//        16 M rows (rows past B read a duplicate activation and are ignored).  This fp32
+//        sum of the halves is the exact value before the format's fp16 rounding; it
+//        differs from the rounded codebook value by at most half an fp16 ulp.
+// 2. gemv_finish_kernel: one workgroup per column block adds its partials in workgroup
+//    order (deterministic), applies the output Hadamard, the scales and the exact 1/128
+//    that replaces the two 1/sqrt(128) factors, and writes fp16 y.
 #include <cstdlib>
 
 #include "launch.h"
@@ -43,45 +44,37 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxB = 8;
-constexpr int kSuper = 4;        // units whose input rotation is done together
-constexpr int kPrefetch = 3;     // units in flight per wave
-constexpr int kTileStride = 36;  // LDS words per staged tile: 4 + 8K (K <= 4)
-// Counter slots live at a fixed place in the workspace whatever the problem shape, so the
-// partial sums of one call can never land on the counters of a later, larger call.
-constexpr int kMaxColumnBlocks = 65536;
+constexpr int kMaxTasks = 4;     // (unit, batch row) rotations per wave and sub-range
+constexpr int kABudget = 32768;  // LDS bytes for A operands
 
 struct GemvParams {
   GemvLaunch L;
   uint32_t *errword;
-  uint32_t *counters;
   float *partials;
-  int U;  // total units
-  int G;  // workgroups
+  int U;   // total units
+  int G;   // workgroups of the partial kernel
   int nI, nJ, maxseg;
+  int kA;  // units per sub-range (A-operand capacity)
 };
 
 // Dynamic LDS layout for batch B.
 struct Lds {
-  uint32_t *a;      // [kSuper][8 tile rows][4 groups][B][4 words]
-  uint32_t *tiles;  // [kWaves][16 tiles][kTileStride]
+  uint32_t *a;      // [kA][8 tile rows][4 groups][B][4 words]
+  uint32_t *tiles;  // [kWaves][kRingBytes / 4]: each wave's code ring
   float *red;       // [kWaves][B][128]
-  float *fin;       // [B][128]
-  int *flag;
 };
 
-__host__ __device__ constexpr size_t lds_a_bytes(int B) { return (size_t)kSuper * 8 * 4 * B * 16; }
-__host__ __device__ constexpr size_t lds_tiles_bytes() { return (size_t)kWaves * 16 * kTileStride * 4; }
-__host__ __device__ constexpr size_t lds_bytes(int B) {
-  return lds_a_bytes(B) + lds_tiles_bytes() + (size_t)kWaves * B * 128 * 4 + (size_t)B * 128 * 4 + 16;
+__host__ __device__ constexpr size_t lds_a_bytes(int B, int kA) { return (size_t)kA * 8 * 4 * B * 16; }
+__host__ __device__ constexpr size_t lds_tiles_bytes() { return (size_t)kWaves * 8192; }
+__host__ __device__ constexpr size_t lds_bytes(int B, int kA) {
+  return lds_a_bytes(B, kA) + lds_tiles_bytes() + (size_t)kWaves * B * 128 * 4;
 }
 
-__device__ __forceinline__ Lds lds_carve(char *base, int B) {
+__device__ __forceinline__ Lds lds_carve(char *base, int B, int kA) {
   Lds s;
   s.a = reinterpret_cast<uint32_t *>(base);
-  s.tiles = reinterpret_cast<uint32_t *>(base + lds_a_bytes(B));
-  s.red = reinterpret_cast<float *>(base + lds_a_bytes(B) + lds_tiles_bytes());
-  s.fin = s.red + kWaves * B * 128;
-  s.flag = reinterpret_cast<int *>(s.fin + B * 128);
+  s.tiles = reinterpret_cast<uint32_t *>(base + lds_a_bytes(B, kA));
+  s.red = reinterpret_cast<float *>(base + lds_a_bytes(B, kA) + lds_tiles_bytes());
   return s;
 }
 
@@ -119,22 +112,9 @@ __device__ __forceinline__ Problem get_problem(const GemvParams &P, int p) {
   return r;
 }
 
-struct Coords {
-  int q, I, p, J;
-};
-
-__device__ __forceinline__ Coords unit_coords(const GemvParams &P, int u) {
-  Coords c;
-  c.q = (int)((unsigned)u / (unsigned)P.nI);
-  c.I = u - c.q * P.nI;
-  c.p = (int)((unsigned)c.q / (unsigned)P.nJ);
-  c.J = c.q - c.p * P.nJ;
-  return c;
-}
-
 // First unit of workgroup g, and the workgroup owning unit u (largest g with start(g) <= u).
-__device__ __forceinline__ int wg_start(int g, int U, int G) { return (int)(((long long)g * U) / G); }
-__device__ __forceinline__ int owner(int u, int U, int G) {
+__host__ __device__ __forceinline__ int wg_start(int g, int U, int G) { return (int)(((long long)g * U) / G); }
+__host__ __device__ __forceinline__ int owner(int u, int U, int G) {
   return (int)((((long long)u + 1) * G - 1) / U);
 }
 
@@ -147,46 +127,42 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // ---------------------------------------------------------------------------------------
-// Input rotation of units [u, u + n) into the A-operand buffer (whole workgroup).
-// a[((s*8 + ti)*4 + g)*B + m] holds, for tile row ti of unit s and batch row m, the four
-// words for rows (2g, 2g+1, 2g+8, 2g+9), each word the fp16 value twice.
+// Input rotation.  a[((s*8 + ti)*4 + g)*B + m] holds, for tile row ti of unit s and batch
+// row m, the four words for rows (2g, 2g+1, 2g+8, 2g+9), each word the fp16 value twice.
+// The loads of a sub-range's rotation are issued before its first code loads (vector
+// memory completions are counted in issue order), the arithmetic runs after.
 // ---------------------------------------------------------------------------------------
-__device__ void rotate_units(const GemvParams &P, int u, int n, const Lds &sm) {
-  const int B = P.L.B, in = P.L.in_features;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int task = wave; task < n * B; task += kWaves) {
-    const int s = task / B, b = task - s * B;
-    const Coords c = unit_coords(P, u + s);
-    const Problem pr = get_problem(P, c.p);
-    float va = 0.f, vb = 0.f;
-    if (pr.ok) {
-      const uint16_t *x = P.L.x + (P.L.x_per_problem ? (size_t)c.p * B * in : (size_t)0) + (size_t)b * in;
-      const int k0 = c.I * 128 + lane, k1 = k0 + 64;
-      va = h2f(ldg(x + k0)) * h2f(ldg(pr.rin + k0));
-      vb = h2f(ldg(x + k1)) * h2f(ldg(pr.rin + k1));
-      if (pr.s_in) { va *= ldg(pr.s_in + k0); vb *= ldg(pr.s_in + k1); }
-      wave_fwht128(va, vb);
-    }
-    // element k = lane (+64): tile row ti = k >> 4, in-tile row rr = k & 15
+struct RotLoads {
+  float x0[kMaxTasks], x1[kMaxTasks], r0[kMaxTasks], r1[kMaxTasks], s0[kMaxTasks], s1[kMaxTasks];
+};
+
+__device__ __forceinline__ void rotation_compute(int B, int n, int wave, const RotLoads &rl, const Lds &sm) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int ti = (lane >> 4) + 4 * h, rr = lane & 15;
-      const int g = (rr & 7) >> 1, w = 2 * (rr >> 3) + (rr & 1);
-      const uint32_t hv = f2h(h ? vb : va);
-      sm.a[((((s * 8 + ti) * 4 + g) * B + b) << 2) + w] = hv | (hv << 16);
+  for (int t = 0; t < kMaxTasks; ++t) {
+    const int task = wave + kWaves * t;
+    if (task < n * B) {
+      const int s = task / B, b = task - s * B;
+      float va = rl.x0[t] * rl.r0[t] * rl.s0[t];
+      float vb = rl.x1[t] * rl.r1[t] * rl.s1[t];
+      wave_fwht128(va, vb);
+      // element k = lane (+64): tile row ti = k >> 4, in-tile row rr = k & 15
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ti = (lane >> 4) + 4 * h, rr = lane & 15;
+        const int g = (rr & 7) >> 1, w = 2 * (rr >> 3) + (rr & 1);
+        const uint32_t hv = f2h(h ? vb : va);
+        sm.a[((((s * 8 + ti) * 4 + g) * B + b) << 2) + w] = hv | (hv << 16);
+      }
     }
   }
 }
 
-// ---------------------------------------------------------------------------------------
 // End of a segment (the workgroup's share of column block q): reduce the waves'
-// accumulators, publish the partial, and let the last contributor finish the block.
-// ---------------------------------------------------------------------------------------
-__device__ void finish_segment(const GemvParams &P, const Lds &sm, const Coords &c, const Problem &pr,
-                               floatx4 (&acc)[8]) {
-  const int B = P.L.B, out = P.L.out_features;
+// accumulators and store the partial (not waited for: loads in flight keep streaming).
+__device__ __forceinline__ void publish_partial(const GemvParams &P, const Lds &sm, int q, floatx4 (&acc)[8]) {
+  const int B = P.L.B;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = blockIdx.x;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int mrow = 4 * (lane >> 4) + r;
@@ -195,152 +171,167 @@ __device__ void finish_segment(const GemvParams &P, const Lds &sm, const Coords 
       for (int jj = 0; jj < 8; ++jj) sm.red[(wave * B + mrow) * 128 + 16 * jj + (lane & 15)] = acc[jj][r];
     }
   }
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
-  const int seg = c.q - wg_start(g, P.U, P.G) / P.nI;
+  const int g = blockIdx.x;
+  const int seg = q - wg_start(g, P.U, P.G) / P.nI;
   float *part = P.partials + ((size_t)g * P.maxseg + seg) * kMaxB * 128;
   for (int idx = tid; idx < B * 128; idx += kThreads) {
     float v = sm.red[idx];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) v += sm.red[w * B * 128 + idx];
-    __hip_atomic_store(part + idx, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
-  __syncthreads();
-  const int g_lo = owner(c.q * P.nI, P.U, P.G), g_hi = owner((c.q + 1) * P.nI - 1, P.U, P.G);
-  if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(P.counters + c.q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *sm.flag = (old == (uint32_t)(g_hi - g_lo));
+    part[idx] = v;
   }
   __syncthreads();
-  if (*sm.flag) {
-    for (int idx = tid; idx < B * 128; idx += kThreads) {
-      float v = 0.f;
-      for (int gg = g_lo; gg <= g_hi; ++gg) {
-        const int sg = c.q - wg_start(gg, P.U, P.G) / P.nI;
-        v += __hip_atomic_load(P.partials + ((size_t)gg * P.maxseg + sg) * kMaxB * 128 + idx,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      sm.fin[idx] = v;
-    }
-    __syncthreads();
-    uint16_t *y = P.L.y + (size_t)c.p * B * out;
-    for (int b = wave; b < B; b += kWaves) {
-      const int c0 = c.J * 128 + lane, c1 = c0 + 64;
-      float va = sm.fin[b * 128 + lane], vb = sm.fin[b * 128 + lane + 64];
-      if (pr.ok) {
-        wave_fwht128(va, vb);
-        float sa = h2f(ldg(pr.rout + c0)) * (1.0f / 128.0f), sb = h2f(ldg(pr.rout + c1)) * (1.0f / 128.0f);
-        if (pr.s_out) { sa *= ldg(pr.s_out + c0); sb *= ldg(pr.s_out + c1); }
-        va *= sa;
-        vb *= sb;
-      } else {
-        va = 0.f;
-        vb = 0.f;
-      }
-      y[(size_t)b * out + c0] = f2h(va);
-      y[(size_t)b * out + c1] = f2h(vb);
-    }
-    if (tid == 0) __hip_atomic_store(P.counters + c.q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
 }
 
 // ---------------------------------------------------------------------------------------
-// Per-lane geometry of the coalesced loads of one unit (two tile rows x 8 tiles per wave).
+// Code streaming.  Each wave owns a ring of kRingBytes of LDS holding whole units (its two
+// tile rows x 8 tiles: 16 tiles, row-major, tile (r, t) at word (8r + t) * 8K).  The rows
+// are copied straight from global memory into the ring with global_load_lds (no register
+// staging), so many units are in flight per wave.  These copies are not tracked by the
+// compiler's wait-count insertion: the loop waits for them itself with s_waitcnt vmcnt(N),
+// issuing exactly kDma copies per unit on every path (dummy copies past the end) so that N
+// is a compile-time constant.  Vector memory operations complete in issue order.
 // ---------------------------------------------------------------------------------------
-template <int K>
-struct UnitLoader {
-  static constexpr int NW = 8 * K;     // words per tile
-  static constexpr int ROWW = 8 * NW;  // words per 8-tile row chunk
-  uint32_t off[K];                     // word offset of the lane's piece t from the unit base
-  uint32_t lds[K];                     // LDS word index of piece t in the wave's tile buffer
-  bool prefix[K];                      // piece t ends with the tile's last word
+constexpr int kRingBytes = 8192;
 
-  __device__ __forceinline__ void init(int lane, int row_stride_words) {
-#pragma unroll
-    for (int t = 0; t < K; ++t) {
-      const int wpos = 2 * (lane + 64 * t);  // word position in the 2-row concatenation
-      const int r = wpos / ROWW, o = wpos - r * ROWW;
-      const int tt = o / NW, dd = o - tt * NW;
-      off[t] = (uint32_t)(r * row_stride_words + o);
-      lds[t] = (uint32_t)((r * 8 + tt) * kTileStride + 4 + dd);
-      prefix[t] = (dd + 1 == NW - 1);
-    }
-  }
+template <int K>
+struct Ring {
+  static constexpr int NW = 8 * K;                      // words per tile
+  static constexpr int UNIT_BYTES = 16 * NW * 4;       // 1024 / 1536 / 2048
+  static constexpr int SLOTS = kRingBytes / UNIT_BYTES; // 8 / 5 / 4
+  static constexpr int DMA = (K == 2) ? 1 : 2;          // copies per unit
+  static constexpr int WAIT = DMA * (SLOTS - 1);        // copies younger than the unit in use
+  static_assert(WAIT < 64, "vmcnt range");
 };
 
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n only.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int imm = (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(imm);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+typedef __attribute__((address_space(3))) void *lds_void_ptr;
+
+// Copy the wave's two tile rows of the unit whose rows start at `row0` (global words) into
+// ring slot `dst` (LDS).  `real` = false: every lane reads the first 16 bytes of `row0`.
 template <int K>
-__device__ __forceinline__ void load_unit(uint32_t (&buf)[2 * K], const uint32_t *base, const UnitLoader<K> &ld) {
+__device__ __forceinline__ void dma_unit(const uint32_t *row0, size_t row_stride_words, uint32_t *dst, bool real) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (K == 2) {
+    // 2 x 512 B: lanes 0..31 take row 0, lanes 32..63 row 1, 16 B each
+    const uint32_t *src = row0 + (real ? ((size_t)(lane >> 5) * row_stride_words + 4 * (lane & 31)) : 0);
+    __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_ptr)dst, 16, 0, 0);
+  } else if constexpr (K == 3) {
+    // 2 x 768 B = 96 pieces of 16 B: lanes 0..63 take pieces 0..63, then lanes 0..31 take
+    // pieces 64..95 (a piece never straddles the two rows: 768 is a multiple of 16)
 #pragma unroll
-  for (int t = 0; t < K; ++t) {
-    const u32x2 v = ldg(reinterpret_cast<const u32x2 *>(base + ld.off[t]));
-    buf[2 * t] = v[0];
-    buf[2 * t + 1] = v[1];
+    for (int c = 0; c < 2; ++c) {
+      const int piece = 64 * c + lane;
+      const int r = piece / 48, w = 4 * (piece - 48 * r);
+      const uint32_t *src = row0 + (real ? ((size_t)r * row_stride_words + w) : 0);
+      if (c == 0 || lane < 32)
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_ptr)(dst + c * 256), 16, 0, 0);
+    }
+  } else {
+    // 2 x 1024 B: one copy per row, 16 B per lane
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const uint32_t *src = row0 + (real ? ((size_t)r * row_stride_words + 4 * lane) : 0);
+      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_ptr)(dst + r * 256), 16, 0, 0);
+    }
   }
 }
 
-// Units [ub, ue) of this workgroup, all of width K.
+// Units [ub, ue) of problem p (width K), in sub-ranges of at most P.kA units.  Each
+// sub-range issues its rotation loads and its first code copies, rotates while the code is
+// in flight, then streams with SLOTS - 1 units in flight per wave.
 template <int K>
-__device__ void run_range(const GemvParams &P, const Lds &sm, int ub, int ue) {
-  constexpr int NW = 8 * K;
-  const int n = ue - ub;
+__device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &pr, int p, int ub, int ue) {
+  using RG = Ring<K>;
+  constexpr int NW = RG::NW;
+  constexpr int SLOTS = RG::SLOTS;
   const int B = P.L.B;
   const int Tj = P.L.out_features / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nI = P.nI;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, grp = lane >> 4;
   const LaneWindow lw = lane_window(lane, K);
-  // first word of the lane's pair inside the staged tile (the prefix copy sits at index 3)
-  const uint32_t wbase = 4u + ((lw.d0 == (uint32_t)(NW - 1)) ? 0xFFFFFFFFu : lw.d0);
-  uint32_t *tb = sm.tiles + wave * 16 * kTileStride;
-  UnitLoader<K> ld;
-  ld.init(lane, Tj * NW);
+  uint32_t *ring = sm.tiles + wave * (kRingBytes / 4);
+  const int mc = m < B ? m : B - 1;  // batch row of the A operand (rows past B are ignored)
+  const uint32_t a_lane = (uint32_t)((grp * B + mc) << 2);
+  const size_t row_stride = (size_t)Tj * NW;
+  const uint32_t *code = pr.code + (size_t)(2 * wave) * row_stride;
+  const size_t row_block_words = 8 * row_stride;
+  const int first = __builtin_amdgcn_readfirstlane(ub - p * P.nI * P.nJ);
+  const int total = __builtin_amdgcn_readfirstlane(ue - ub);
+  const int in = P.L.in_features;
+  const uint16_t *xp = P.L.x + (P.L.x_per_problem ? (size_t)p * B * in : (size_t)0);
 
-  auto unit_base = [&](int u) -> const uint32_t * {
-    const Coords c = unit_coords(P, u);
-    const Problem pr = get_problem(P, c.p);
-    return pr.code + ((size_t)(8 * c.I + 2 * wave) * Tj + (size_t)8 * c.J) * NW;
-  };
-
-  uint32_t ring[kPrefetch][2 * K];
-#pragma unroll
-  for (int j = 0; j < kPrefetch; ++j)
-    if (j < n) load_unit<K>(ring[j], unit_base(ub + j), ld);
   floatx4 acc[8];
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < n; k0 += kPrefetch) {
+  for (int sb = 0; sb < total; sb += P.kA) {
+    const int n = __builtin_amdgcn_readfirstlane(min(P.kA, total - sb));
+    int cur_I = __builtin_amdgcn_readfirstlane((first + sb) % nI);
+    int cur_J = __builtin_amdgcn_readfirstlane((first + sb) / nI);
+    int pre_I = cur_I, pre_J = cur_J;
+    RotLoads rq;
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) {
-      const int k = k0 + j;
-      if (k >= n) break;
-      // input rotation for the next kSuper units
-      if (k % kSuper == 0) {
-        __syncthreads();
-        rotate_units(P, ub + k, min(kSuper, n - k), sm);
-        __syncthreads();
+    for (int t = 0; t < kMaxTasks; ++t) {
+      const int task = wave + kWaves * t;
+      if (task < n * B) {
+        const int s = task / B, b = task - s * B;
+        const int I = (first + sb + s) % nI;
+        const int k0 = I * 128 + lane, k1 = k0 + 64;
+        rq.x0[t] = h2f(ldg(xp + (size_t)b * in + k0));
+        rq.x1[t] = h2f(ldg(xp + (size_t)b * in + k1));
+        rq.r0[t] = h2f(ldg(pr.rin + k0));
+        rq.r1[t] = h2f(ldg(pr.rin + k1));
+        rq.s0[t] = pr.s_in ? ldg(pr.s_in + k0) : 1.f;
+        rq.s1[t] = pr.s_in ? ldg(pr.s_in + k1) : 1.f;
       }
-      // stage unit k's words in the wave's LDS buffer
+    }
+    // the previous sub-range's reads of the A buffer and of the ring are finished
+    __syncthreads();
+    // first SLOTS-1 units into slots 0..SLOTS-2
 #pragma unroll
-      for (int t = 0; t < K; ++t) {
-        *reinterpret_cast<u32x2 *>(tb + ld.lds[t]) = u32x2{ring[j][2 * t], ring[j][2 * t + 1]};
-        if (ld.prefix[t]) tb[ld.lds[t] - 4 - (NW - 2) + 3] = ring[j][2 * t + 1];
+    for (int j = 0; j < SLOTS - 1; ++j) {
+      const bool real = j < n;
+      dma_unit<K>(code + (size_t)pre_I * row_block_words + (size_t)(8 * pre_J) * NW, row_stride,
+                  ring + j * (RG::UNIT_BYTES / 4), real);
+      if (real && ++pre_I == nI) { pre_I = 0; ++pre_J; }
+    }
+    rotation_compute(B, n, wave, rq, sm);
+    __syncthreads();
+
+    int slot = 0;
+    for (int k = 0; k < n; ++k) {
+      // copy unit k + SLOTS - 1 into the slot unit k - 1 used (its reads are complete)
+      {
+        const int ws = (slot == 0 ? SLOTS : slot) - 1;
+        const bool real = k + SLOTS - 1 < n;
+        const uint32_t *row0 = real ? code + (size_t)pre_I * row_block_words + (size_t)(8 * pre_J) * NW : code;
+        dma_unit<K>(row0, row_stride, ring + ws * (RG::UNIT_BYTES / 4), real);
+        if (real && ++pre_I == nI) { pre_I = 0; ++pre_J; }
       }
-      // refill this ring slot with unit k + kPrefetch
-      if (k + kPrefetch < n) load_unit<K>(ring[j], unit_base(ub + k + kPrefetch), ld);
-      wave_sync();
-      const int s = k % kSuper;
+      wait_vmcnt<RG::WAIT>();  // unit k has landed
+      const uint32_t *ub_ = ring + slot * (RG::UNIT_BYTES / 4);
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        u32x4 a = {0u, 0u, 0u, 0u};
-        if (m < B) a = *reinterpret_cast<const u32x4 *>(sm.a + ((((s * 8 + 2 * wave + r) * 4 + grp) * B + m) << 2));
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(sm.a + (uint32_t)(((k * 8 + 2 * wave + r) * 4 * B) << 2) + a_lane);
         const half8 av = __builtin_bit_cast(half8, a);
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
-          const uint32_t *tw = tb + (r * 8 + tt) * kTileStride + wbase;
-          const uint32_t bits = lane_bits(tw[0], tw[1], lw.sh);
+          const uint32_t *tw = ub_ + (r * 8 + tt) * NW;
+          const uint32_t bits = lane_bits(tw[lw.d0], tw[lw.d1], lw.sh);
           u32x4 bw;
           bw[0] = mcg_hash(lane_state<K>(bits, 0));
           bw[1] = mcg_hash(lane_state<K>(bits, 1));
@@ -350,58 +341,108 @@ __device__ void run_range(const GemvParams &P, const Lds &sm, int ub, int ue) {
         }
       }
       wave_sync();
-      const Coords c = unit_coords(P, ub + k);
-      if (c.I == P.nI - 1 || k == n - 1) {
-        const Problem pr = get_problem(P, c.p);
-        finish_segment(P, sm, c, pr, acc);
-      }
+      if (cur_I == nI - 1 || sb + k == total - 1) publish_partial(P, sm, p * P.nJ + cur_J, acc);
+      if (++cur_I == nI) { cur_I = 0; ++cur_J; }
+      slot = (slot + 1 == SLOTS) ? 0 : slot + 1;
     }
+    wait_vmcnt<0>();  // the dummy copies of the tail have landed before the ring is reused
   }
 }
 
-// Units of invalid problems: no loads; every segment publishes a zero partial so the column
-// blocks still complete (with zero output) and the error word is set.
+// Units of invalid problems: no loads; each segment publishes a zero partial (the finishing
+// kernel writes zeros for invalid problems anyway) and the error word is set.
 __device__ void run_invalid(const GemvParams &P, const Lds &sm, int ub, int ue) {
   if (threadIdx.x == 0) __hip_atomic_fetch_or(P.errword, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   floatx4 acc[8];
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
   for (int u = ub; u < ue; ++u) {
-    const Coords c = unit_coords(P, u);
-    if (c.I == P.nI - 1 || u == ue - 1) {
-      const Problem pr = get_problem(P, c.p);
-      finish_segment(P, sm, c, pr, acc);
-    }
+    const int q = u / P.nI, I = u - q * P.nI;
+    if (I == P.nI - 1 || u == ue - 1) publish_partial(P, sm, q, acc);
   }
 }
 
-__device__ __forceinline__ int problem_class(const GemvParams &P, int p) {
-  const Problem pr = get_problem(P, p);
-  return pr.ok ? pr.K : 0;
-}
-
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams P) {
+__global__ __launch_bounds__(kThreads, 4) void gemv_partial_kernel(GemvParams P) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
-  const Lds sm = lds_carve(lds_raw, P.L.B);
+  const Lds sm = lds_carve(lds_raw, P.L.B, P.kA);
   const int g = blockIdx.x;
   const int u0 = wg_start(g, P.U, P.G), u1 = wg_start(g + 1, P.U, P.G);
   const int per_problem = P.nI * P.nJ;
-  int u = u0;
-  while (u < u1) {
-    int p = u / per_problem;
-    const int cls = problem_class(P, p);
-    int ue = min(u1, (p + 1) * per_problem);
-    while (ue < u1 && problem_class(P, p + 1) == cls) {
-      ++p;
-      ue = min(u1, (p + 1) * per_problem);
-    }
-    switch (cls) {
-      case 2: run_range<2>(P, sm, u, ue); break;
-      case 3: run_range<3>(P, sm, u, ue); break;
-      case 4: run_range<4>(P, sm, u, ue); break;
+  for (int u = u0; u < u1;) {
+    const int p = u / per_problem;
+    const int ue = min(u1, (p + 1) * per_problem);
+    const Problem pr = get_problem(P, p);
+    switch (pr.ok ? pr.K : 0) {
+      case 2: run_problem<2>(P, sm, pr, p, u, ue); break;
+      case 3: run_problem<3>(P, sm, pr, p, u, ue); break;
+      case 4: run_problem<4>(P, sm, pr, p, u, ue); break;
       default: run_invalid(P, sm, u, ue); break;
     }
     u = ue;
+  }
+}
+
+// One workgroup per column block q: sum the contributors' partials in workgroup order,
+// rotate, scale and write fp16 y.
+constexpr int kPartialBatch = 16;  // partial loads a thread issues together
+
+__global__ __launch_bounds__(kThreads) void gemv_finish_kernel(GemvParams P) {
+  __shared__ float fin[kMaxB][128];
+  __shared__ int slot_of[kPartialBatch];
+  const int B = P.L.B, out = P.L.out_features;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = blockIdx.x;
+  const int g_lo = owner(q * P.nI, P.U, P.G), g_hi = owner((q + 1) * P.nI - 1, P.U, P.G);
+  float v[kMaxB * 128 / kThreads];
+#pragma unroll
+  for (int i = 0; i < kMaxB * 128 / kThreads; ++i) v[i] = 0.f;
+  for (int gb = g_lo; gb <= g_hi; gb += kPartialBatch) {
+    // partial slot of each contributor of this batch (index arithmetic fits in 32 bits)
+    __syncthreads();
+    if (tid < kPartialBatch) {
+      const int gg = gb + tid;
+      slot_of[tid] = gg <= g_hi ? gg * P.maxseg + (q - (int)((unsigned)(gg * P.U) / (unsigned)P.G) / P.nI) : -1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kMaxB * 128 / kThreads; ++i) {
+      const int idx = tid + i * kThreads;
+      if (idx < B * 128) {
+        float part[kPartialBatch];
+#pragma unroll
+        for (int t = 0; t < kPartialBatch; ++t) {
+          const int sl = slot_of[t];
+          part[t] = sl >= 0 ? P.partials[(size_t)sl * kMaxB * 128 + idx] : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < kPartialBatch; ++t) v[i] += part[t];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxB * 128 / kThreads; ++i) {
+    const int idx = tid + i * kThreads;
+    if (idx < B * 128) fin[idx >> 7][idx & 127] = v[i];
+  }
+  __syncthreads();
+  const int p = q / P.nJ, J = q - p * P.nJ;
+  const Problem pr = get_problem(P, p);
+  uint16_t *y = P.L.y + (size_t)p * B * out;
+  for (int b = wave; b < B; b += kWaves) {
+    const int c0 = J * 128 + lane, c1 = c0 + 64;
+    float va = fin[b][lane], vb = fin[b][lane + 64];
+    if (pr.ok) {
+      wave_fwht128(va, vb);
+      float sa = h2f(ldg(pr.rout + c0)) * (1.0f / 128.0f), sb = h2f(ldg(pr.rout + c1)) * (1.0f / 128.0f);
+      if (pr.s_out) { sa *= ldg(pr.s_out + c0); sb *= ldg(pr.s_out + c1); }
+      va *= sa;
+      vb *= sb;
+    } else {
+      va = 0.f;
+      vb = 0.f;
+    }
+    y[(size_t)b * out + c0] = f2h(va);
+    y[(size_t)b * out + c1] = f2h(vb);
   }
 }
 
@@ -422,7 +463,8 @@ int device_cus_and_occupancy(int B, int *cus_out) {
   }
   if (d.occ[B] == 0) {
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_kernel, kThreads, lds_bytes(B)) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_partial_kernel, kThreads,
+                                                     lds_bytes(B, kWaves * kMaxTasks / B)) != hipSuccess ||
         occ <= 0)
       occ = 2;
     d.occ[B] = occ;
@@ -432,8 +474,8 @@ int device_cus_and_occupancy(int B, int *cus_out) {
 }
 
 struct Geometry {
-  int U, G, nI, nJ, maxseg, nq;
-  size_t counters_off, partials_off, bytes;
+  int U, G, nI, nJ, maxseg, nq, kA;
+  size_t partials_off, bytes;
 };
 
 Geometry geometry(int n_problems, int in_features, int out_features, int B) {
@@ -456,15 +498,17 @@ Geometry geometry(int n_problems, int in_features, int out_features, int B) {
   gm.G = (int)G;
   const long long per = (U + G - 1) / G;
   gm.maxseg = (int)((per + gm.nI - 1) / gm.nI + 1);
-  gm.counters_off = 256;
-  gm.partials_off = gm.counters_off + (size_t)kMaxColumnBlocks * 4;
+  long long kA_max = kABudget / (512 * B);
+  if (kA_max > (long long)kWaves * kMaxTasks / B) kA_max = (long long)kWaves * kMaxTasks / B;
+  gm.kA = (int)(per < kA_max ? per : kA_max);
+  gm.partials_off = 256;
   gm.bytes = gm.partials_off + (size_t)gm.G * gm.maxseg * kMaxB * 128 * sizeof(float);
   return gm;
 }
 
 }  // namespace
 
-int gemv_max_column_blocks() { return kMaxColumnBlocks; }
+int gemv_max_column_blocks() { return 1 << 30; }
 
 size_t gemv_workspace_bytes(int n_problems, int in_features, int out_features, int B) {
   if (n_problems <= 0) return 256;
@@ -479,20 +523,23 @@ hipError_t launch_gemv(const GemvLaunch &a, void *ws, size_t ws_bytes, hipStream
   const long long units = (long long)a.n_problems * (a.out_features / 128) * (a.in_features / 128);
   if (units >= (1LL << 31)) return hipErrorInvalidValue;
   const Geometry gm = geometry(a.n_problems, a.in_features, a.out_features, a.B);
-  if (gm.nq > kMaxColumnBlocks) return hipErrorInvalidValue;
   if (ws_bytes < gm.bytes) return hipErrorInvalidValue;
+  if ((long long)gm.G * gm.U >= (1LL << 32)) return hipErrorInvalidValue;  // 32-bit slot arithmetic
   GemvParams P;
   P.L = a;
   char *w = static_cast<char *>(ws);
   P.errword = reinterpret_cast<uint32_t *>(w);
-  P.counters = reinterpret_cast<uint32_t *>(w + gm.counters_off);
   P.partials = reinterpret_cast<float *>(w + gm.partials_off);
   P.U = gm.U;
   P.G = gm.G;
   P.nI = gm.nI;
   P.nJ = gm.nJ;
   P.maxseg = gm.maxseg;
-  gemv_kernel<<<gm.G, kThreads, lds_bytes(a.B), stream>>>(P);
+  P.kA = gm.kA;
+  gemv_partial_kernel<<<gm.G, kThreads, lds_bytes(a.B, gm.kA), stream>>>(P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  gemv_finish_kernel<<<gm.nq, kThreads, 0, stream>>>(P);
   return hipGetLastError();
 }
 
