@@ -27,6 +27,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 ROTATE_BYTES = 1 << 30
+COPY_PROBE_BYTES = 256 << 20   # plain device copy used to calibrate the HBM byte counters
+# Counter-derived HBM traffic of the GEMV launch, with the hash of the kernel sources it was
+# measured on; the figure is reported only while those sources are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_dense_mlp_b1_hbm_traffic.txt")
+GEMV_SOURCES = ["trellis_coded_bit_amd/csrc/gemv.hip", "trellis_coded_bit_amd/csrc/trellis_device.h",
+                "trellis_coded_bit_amd/csrc/launch.h"]
 
 
 def _log(msg):
@@ -66,6 +72,44 @@ def cpu_baseline_dense(wl, budget_s: float = 12.0):
                       f"{platform.processor() or platform.machine()}, os.cpu_count()={os.cpu_count()}, "
                       f"affinity={len(os.sched_getaffinity(0))}, numpy decode single-threaded, "
                       f"BLAS threads={blas_threads}"}
+
+
+def gemv_source_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per GEMV launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE,
+    each scaled by the same counter's reading for a plain copy of known size), or None when
+    the summary is missing or was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(line.split(":", 1) for line in fh if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha256") != gemv_source_sha256():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(torch):
+    """Three plain device-to-device copies of COPY_PROBE_BYTES (the counter calibration)."""
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"bytes_read_per_copy": COPY_PROBE_BYTES, "bytes_written_per_copy": COPY_PROBE_BYTES, "copies": 3}
 
 
 def _capture(torch, fn):
@@ -144,7 +188,8 @@ def run_dense(args, torch, tb, synth):
                    "global_batch": 1, "code_bytes_per_step": code_bytes, "weight_copies_rotated": R,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic()},
+        "algorithmic_bytes_per_launch": code_bytes / 3,
         "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
         "effective_weight_tflops": round(flops / (ms_step * 1e-3) / 1e12, 3),
         "gemv_launch_us": {k: round(v, 2) for k, v in per_matrix_us.items()},
@@ -258,6 +303,8 @@ def main():
     ap.add_argument("--workload", default="dense", choices=["dense", "small_batch", "moe", "prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -274,6 +321,8 @@ def main():
         out, wl = run_dense(args, torch, tb, synth)
         if not args.no_prefill:
             out["prefill"] = run_prefill(args, torch, tb, synth)
+        if args.copy_probe:
+            out["copy_probe"] = copy_probe(torch)
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline_dense(wl)
         print(json.dumps(out), flush=True)
