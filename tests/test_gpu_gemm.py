@@ -24,6 +24,21 @@ def test_gemm_small_shapes(K, M, n_in, n_out):
     assert rel_l2(y.cpu().numpy(), ref) < REL_L2_TOL
 
 
+@pytest.mark.parametrize("wgs", [1, 3, 7, 16, 61])
+def test_gemm_stream_k_splits(wgs, monkeypatch):
+    """Forced workgroup counts move the range boundaries: one range over every tile, ranges
+    over several tiles, ranges inside one tile, one k-step pair per range.  Every split of
+    the k-sum must still give the oracle's product (M = 300: a ragged second row band)."""
+    monkeypatch.setenv("TRELLIS_GEMM_WGS", str(wgs))
+    log_case(f"gemm stream-K wgs={wgs}")
+    lin = synth.make_linear(np.random.SeedSequence([77, wgs]), 3, 384, 512)
+    x = synth.make_x(np.random.SeedSequence(78), 300, 384)
+    y = tb.trellis_gemm(dev_linear(lin), to_dev(x))
+    torch.cuda.synchronize()
+    ref = O.forward_linear(lin, x)
+    assert rel_l2(y.cpu().numpy(), ref) < REL_L2_TOL
+
+
 def test_gemm_prefill_full_size_sampled():
     """K3 5120 -> 17408 with M = 2048: full GPU product, oracle on sampled rows x blocks."""
     log_case("gemm prefill full size")

@@ -22,6 +22,8 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 // The MCG hash ("Codebook: cb=1"): v = s * 0xCBAC1FED mod 2^32, then (v & 0x8FFF8FFF) ^
 // 0x3B603B60.  The result, read as two fp16 halves, sums to the codebook value.
@@ -91,22 +93,46 @@ __device__ __forceinline__ uint16_t f2h(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// Unnormalised Sylvester Hadamard butterfly over 128 values held as two per lane
-// (a = element lane, b = element lane + 64) across a full wave of 64 lanes.
-// Produces (H_128 z)[lane] in a and (H_128 z)[lane + 64] in b.
+// Value of lane (lane ^ m) for m = 1, 2, 4, 8 (DPP within rows of 16), 16 (swizzle within
+// halves of the wave) and 32 (bpermute).
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  int r;
+  if constexpr (M == 1) r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  else if constexpr (M == 2) r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  else if constexpr (M == 4)  // row_half_mirror (i -> 7 - i) then quad_perm 3,2,1,0: i -> i ^ 4
+    r = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false), 0x1B, 0xF, 0xF, false);
+  else if constexpr (M == 8) r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror 8
+  else if constexpr (M == 16) r = __builtin_amdgcn_ds_swizzle(x, 0x401F);             // xor 16
+  else r = __shfl_xor(x, M, 64);
+  return __builtin_bit_cast(float, r);
+}
+
+template <int M>
+__device__ __forceinline__ void fwht_stage(float &a, float &b, int lane) {
+  const float pa = lane_xor<M>(a), pb = lane_xor<M>(b);
+  const bool up = (lane & M) != 0;
+  a = up ? (pa - a) : (a + pa);
+  b = up ? (pb - b) : (b + pb);
+}
+
+// Unnormalised Sylvester Hadamard butterfly over 128 values held two per lane: element
+// e = 64*h + lane in (a, b)[h] with the in-register stage pairing h, or any other fixed
+// assignment of the seven index bits to (h, lane bits) -- H_128 is the tensor product of
+// seven 2x2 butterflies, so the stages may run in any order and the output uses the same
+// assignment as the input.
 __device__ __forceinline__ void wave_fwht128(float &a, float &b) {
   const int lane = threadIdx.x & 63;
-  float s = a + b, d = a - b;
+  const float s = a + b, d = a - b;
   a = s;
   b = d;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    float pa = __shfl_xor(a, m, 64);
-    float pb = __shfl_xor(b, m, 64);
-    const bool up = (lane & m) != 0;
-    a = up ? (pa - a) : (a + pa);
-    b = up ? (pb - b) : (b + pb);
-  }
+  fwht_stage<1>(a, b, lane);
+  fwht_stage<2>(a, b, lane);
+  fwht_stage<4>(a, b, lane);
+  fwht_stage<8>(a, b, lane);
+  fwht_stage<16>(a, b, lane);
+  fwht_stage<32>(a, b, lane);
 }
 
 }  // namespace trellis
