@@ -39,6 +39,25 @@ def test_gemm_stream_k_splits(wgs, monkeypatch):
     assert rel_l2(y.cpu().numpy(), ref) < REL_L2_TOL
 
 
+def _offset_copy(a: np.ndarray) -> torch.Tensor:
+    """The same values one element past an allocation's start (2- or 4-byte aligned only)."""
+    buf = torch.empty(a.size + 1, dtype=torch.from_numpy(a).dtype, device="cuda")
+    buf[1:] = torch.from_numpy(a).cuda()
+    return buf[1:]
+
+
+def test_gemm_unaligned_side_vectors():
+    """rin/s_in that are only naturally aligned take the element-load rotation."""
+    lin = synth.make_linear(np.random.SeedSequence(41), 2, 256, 256)
+    x = synth.make_x(np.random.SeedSequence(42), 40, 256)
+    L = tb.TrellisLinear(torch.from_numpy(lin.code).cuda(), _offset_copy(lin.rin), _offset_copy(lin.rout),
+                         _offset_copy(lin.s_in), _offset_copy(lin.s_out), lin.K)
+    assert L.rin.data_ptr() % 16 != 0 and L.s_in.data_ptr() % 16 != 0
+    y = tb.trellis_gemm(L, to_dev(x))
+    torch.cuda.synchronize()
+    assert rel_l2(y.cpu().numpy(), O.forward_linear(lin, x)) < REL_L2_TOL
+
+
 def test_gemm_prefill_full_size_sampled():
     """K3 5120 -> 17408 with M = 2048: full GPU product, oracle on sampled rows x blocks."""
     log_case("gemm prefill full size")

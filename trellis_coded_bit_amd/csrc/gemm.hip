@@ -3,9 +3,9 @@
 // ("Escha-W2 runs on Metal", reconstruction paragraph; decode as in decode.hip.)
 //
 // Three launches:
-//   1. rotate: XH = H128(X*su) (unnormalised butterfly) as fp16 in the workspace, with the
-//      32 input channels of every k-step stored in the order the MFMA operands take them
-//      (below), so every A-operand load is one contiguous 16-byte piece;
+//   1. rotate: XH = H128(X*su) (unnormalised butterfly) as fp16 in the workspace, stored in
+//      1 KB blocks of 16 rows x one k-step laid out exactly as the MFMA A operands are held
+//      by the lanes, so every A-operand load is one contiguous 1 KB piece;
 //   2. the stream-K product.  Output tiles are 256 rows x 128 columns (one Hadamard block)
 //      and a tile's k-steps are 32 input rows (two trellis tile rows).  The (tile, k-step)
 //      iterations are numbered tile-major and every workgroup takes one contiguous range
@@ -37,20 +37,22 @@ namespace trellis {
 
 namespace {
 
-constexpr int kMT = 256;      // output rows per tile
+constexpr int kMT = 512;      // output rows per tile
 constexpr int kNT = 128;      // output columns per tile (one Hadamard block)
 constexpr int kKS = 32;       // input rows per k-step (two trellis tile rows)
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kTileFloats = kMT * kNT;
 constexpr int kMinSteps = 4;  // fewest k-step pairs per workgroup worth a split
 
 struct GemmParams {
-  const uint16_t *xh;  // [M][in] rotated activations, k permuted inside each 32-group
+  const uint16_t *xh;  // rotated activations in 16-row x k-step blocks (rotate_kernel)
   const uint32_t *code;
   const uint16_t *rout;
   const float *s_out;
   uint16_t *y;
   float *partials;     // [2G][kTileFloats]
+  uint32_t *counters;  // [T] arrivals per tile, zeroed by the rotation launch
   int M, in, out;
   int S;               // k-step pairs per tile (the unit of the ranges)
   int nNT;             // column tiles
@@ -74,37 +76,101 @@ __device__ __forceinline__ int xcd_range(int b, int G) {
   return x * (G >> 3) + min(x, G & 7) + j;
 }
 
-// Position, inside a k-step, of input row kk of the step: the MFMA operand element 8*g + j
-// of lane group g holds row 16*(j >> 2) + 2*g + (j & 1) + 8*((j >> 1) & 1), which is the
-// tile row of the decoder's symbol j & 3 in tile row-pair j >> 2 (trellis_device.h).
-__device__ __forceinline__ int kperm_pos(int kk) {
-  return 8 * ((kk >> 1) & 3) + 4 * (kk >> 4) + 2 * ((kk >> 3) & 1) + (kk & 1);
-}
-
-// XH = H128(X*su), one wave per (row, 128-block), k-permuted fp16 output.
+// Layout of the rotated activations XH: blocks of 16 rows x one k-step (32 input rows),
+// 1 KB each, ordered [row block][k-step]; inside a block, MFMA lane l = 16*g + (m & 15)
+// owns 16 contiguous bytes holding its eight A-operand elements j = 0..7, which are the
+// step's input rows 16*(j >> 2) + 2*g + (j & 1) + 8*((j >> 1) & 1) -- the tile rows of the
+// decoder's symbols j & 3 in the step's tile row j >> 2 (trellis_device.h).  Every
+// A-operand load is then one contiguous, fully used 1 KB piece.
+//
+// XH = H128(X*su): a workgroup per (16-row block, 128-column block), 16 lanes per row with
+// 8 consecutive elements each (three in-register butterfly stages, four across the 16
+// lanes).  The 4 KB of output (four consecutive 1 KB k-step blocks) is assembled in LDS and
+// stored with 16 contiguous bytes per thread.  Rows past M are written as zeros.
+// VEC: rin and s_in are 16-byte aligned (vector loads), else element loads.
+template <bool VEC>
 __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t *__restrict__ x, int rows, int n,
                                                      const uint16_t *__restrict__ r,
                                                      const float *__restrict__ s,
-                                                     uint16_t *__restrict__ xh) {
+                                                     uint16_t *__restrict__ xh,
+                                                     uint32_t *__restrict__ counters, int ncounters) {
+  __shared__ __attribute__((aligned(16))) uint16_t stage[4 * 512];
+  for (int c = blockIdx.x * 256 + threadIdx.x; c < ncounters; c += gridDim.x * 256) counters[c] = 0;
   const int nb = n / 128;
-  const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= (long long)rows * nb) return;
-  const int row = (int)(task / nb), blk = (int)(task % nb);
-  const int lane = threadIdx.x & 63;
-  const size_t base = (size_t)row * n + (size_t)blk * 128;
-  const int c0 = blk * 128 + lane, c1 = c0 + 64;
-  float a = h2f(x[base + lane]), b = h2f(x[base + lane + 64]);
-  float sa = h2f(r[c0]), sb = h2f(r[c1]);
-  if (s) {
-    sa *= s[c0];
-    sb *= s[c1];
+  const int rb = blockIdx.x / nb, blk = blockIdx.x - rb * nb;
+  const int q = threadIdx.x >> 4;  // row of the block
+  const int i = threadIdx.x & 15;  // elements 8i .. 8i+7 of the 128-block
+  const int row = 16 * rb + q;
+  const int c = blk * 128 + 8 * i;
+  float v[8];
+  if (row < rows) {
+    const u32x4 xv = *reinterpret_cast<const u32x4 *>(x + (size_t)row * n + c);
+    if (VEC) {
+      const u32x4 rv = *reinterpret_cast<const u32x4 *>(r + c);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t xw = xv[t >> 1], rw = rv[t >> 1];
+        const uint16_t xs = (t & 1) ? (uint16_t)(xw >> 16) : (uint16_t)xw;
+        const uint16_t rs = (t & 1) ? (uint16_t)(rw >> 16) : (uint16_t)rw;
+        v[t] = h2f(xs) * h2f(rs);
+      }
+      if (s) {
+        const floatx4 s0 = *reinterpret_cast<const floatx4 *>(s + c);
+        const floatx4 s1 = *reinterpret_cast<const floatx4 *>(s + c + 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[t] *= s0[t];
+          v[t + 4] *= s1[t];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t xw = xv[t >> 1];
+        const uint16_t xs = (t & 1) ? (uint16_t)(xw >> 16) : (uint16_t)xw;
+        v[t] = h2f(xs) * h2f(r[c + t]);
+        if (s) v[t] *= s[c + t];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = 0.f;
   }
-  a *= sa;
-  b *= sb;
-  wave_fwht128(a, b);
-  const int e0 = lane, e1 = lane + 64;  // block element of a and b
-  xh[base + (e0 & ~31) + kperm_pos(e0 & 31)] = f2h(a);
-  xh[base + (e1 & ~31) + kperm_pos(e1 & 31)] = f2h(b);
+  // element index bits 0..2: register t, bits 3..6: lane i
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if ((t & h) == 0) {
+        const float a = v[t], b = v[t + h];
+        v[t] = a + b;
+        v[t + h] = a - b;
+      }
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    float p;
+    p = lane_xor<1>(v[t]);
+    v[t] = (lane & 1) ? (p - v[t]) : (v[t] + p);
+    p = lane_xor<2>(v[t]);
+    v[t] = (lane & 2) ? (p - v[t]) : (v[t] + p);
+    p = lane_xor<4>(v[t]);
+    v[t] = (lane & 4) ? (p - v[t]) : (v[t] + p);
+    p = lane_xor<8>(v[t]);
+    v[t] = (lane & 8) ? (p - v[t]) : (v[t] + p);
+  }
+  // element 8i + t is row kk = 8*(i & 3) + t of the block's k-step i >> 2: operand group
+  // g = t >> 1, element j = 2*(i & 3) + (t & 1), stored at lane slot 16*g + q
+  uint16_t *dst = stage + (i >> 2) * 512 + q * 8 + 2 * (i & 3);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const half2_t pr = {(_Float16)v[2 * g], (_Float16)v[2 * g + 1]};
+    *reinterpret_cast<half2_t *>(dst + 16 * 8 * g) = pr;
+  }
+  __syncthreads();
+  const int S32 = n / 32;
+  uint16_t *out = xh + ((size_t)rb * S32 + 4 * blk) * 512;
+  reinterpret_cast<u32x4 *>(out)[threadIdx.x] = reinterpret_cast<const u32x4 *>(stage)[threadIdx.x];
 }
 
 // Four symbols of one tile for this lane -> fp16 codebook values packed in pairs
@@ -196,76 +262,114 @@ __device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int m
   }
 }
 
-// Partial tiles: wave-major, then (mb, nb), then lane, four floats each (coalesced).
-__device__ __forceinline__ float *partial_ptr(const GemmParams &P, int slot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return P.partials + (size_t)slot * kTileFloats + (size_t)(wave * 32 * 64 + lane) * 4;
-}
-
 // Raw buffer resource over `bytes` bytes at `base` (loads past the end return zero).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, long long bytes) {
   const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
 }
 
+// Partial tiles in the workspace: slot-major, then wave, (mb, nb), lane, four floats each
+// (coalesced 1 KB per instruction).  They are written and read with device-scope
+// coherence (the sc1 cache policy: through the per-XCD L2s), because the workgroup that
+// adds them may run on another XCD.
+constexpr int kSC1 = 16;  // cache-policy operand of the buffer intrinsics: SC1
+
+__device__ __forceinline__ void store_partial(const GemmParams &P, int slot, const Acc &acc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t rp =
+      buffer_rsrc(P.partials + (size_t)slot * kTileFloats, (long long)kTileFloats * 4);
+  const uint32_t off = (uint32_t)(wave * 32 * 64 + lane) * 16;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+      __builtin_amdgcn_raw_buffer_store_b128(acc[mb][nb], rp, off, (mb * 8 + nb) * 64 * 16, kSC1);
+}
+
+__device__ __forceinline__ void add_partial(const GemmParams &P, int slot, Acc &acc, bool init) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t rp =
+      buffer_rsrc(P.partials + (size_t)slot * kTileFloats, (long long)kTileFloats * 4);
+  const uint32_t off = (uint32_t)(wave * 32 * 64 + lane) * 16;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const floatx4 v = __builtin_amdgcn_raw_buffer_load_b128(rp, off, (mb * 8 + nb) * 64 * 16, kSC1);
+      acc[mb][nb] = init ? v : acc[mb][nb] + v;
+    }
+}
+
 // Accumulates k-step pairs [k0, k1) of tile t (k-steps 2*k0 .. 2*k1 - 1).
 template <int K>
-__device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][64], int t, int k0,
-                                          int k1, Acc &acc) {
+__device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][64],
+                                          u32x4 (*cring)[4 * 2 * 32 / 4], int t, int k0, int k1, Acc &acc) {
   constexpr int NW = 8 * K;  // 32-bit words per trellis tile
-  const int lane = threadIdx.x & 63;
+  // The lane's constants are recomputed per piece rather than kept live across the
+  // epilogue (where they would be spilled and reloaded just before the loop, and the wait
+  // for those reloads would then sit inside the loop).
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int mt = t / P.nNT, nt = t - mt * P.nNT;
   const LaneWindow lw = lane_window(lane, K);
 
-  // A operands: rows 64*wave + 16*mb + (lane & 15) of the tile, 8 halves at 8*(lane >> 4)
-  // of each step.  Rows past M lie past the resource's end and read as zero.
+  // A operands: row blocks row0/16 + mb of XH (rows 64*wave + 16*mb + (lane & 15) of the
+  // tile), one 1 KB block per step.  Blocks past the last row block read as zero.
   const int row0 = mt * kMT + 64 * wave;
-  const __amdgpu_buffer_rsrc_t ra =
-      buffer_rsrc(P.xh + (size_t)row0 * P.in, (long long)(P.M - row0) * P.in * 2);
-  const uint32_t a_off = (uint32_t)(((lane & 15) * P.in + 8 * (lane >> 4)) * 2);
-  const int a_mb = 16 * P.in * 2;  // bytes between m-blocks
-  // Codes: column blocks 2*wave + j of the tile, tile rows 2*step + ti; steps past the end
-  // of the code array read as zero (their results are never used).
+  const int S32 = 2 * P.S;  // k-steps per row block
+  const int Mpad = (P.M + 15) & ~15;
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(P.xh + (size_t)(row0 >> 4) * S32 * 512,
+                                                (long long)(Mpad - row0) * P.in * 2);
+  const uint32_t a_off = (uint32_t)lane * 16;
+  const int a_mb = S32 * 1024;  // bytes between row blocks
+  // Codes: column block `wave` of the tile, tile rows 2*step + ti.  The step's two tiles
+  // (2 * NW words) are loaded with one 4-byte word per lane (lanes past 2 * NW repeat
+  // the first ones) and staged in a wave-private four-step LDS ring, from which every
+  // lane reads the two words of each tile that hold its windows.  Steps past the end of
+  // the code array read as zero (their results are never used).
   const long long row_bytes = (long long)(P.out / 16) * NW * 4;
   const long long code_bytes = (long long)(P.in / 16) * row_bytes;
-  const long long col_off = (long long)(nt * 8 + 2 * wave) * NW * 4;
-  const uint32_t d0 = lw.d0 * 4, d1 = lw.d1 * 4;
+  const long long col_off = (long long)(nt * 8 + wave) * NW * 4;
+  const int cword = lane % (2 * NW);  // word of the step's two tiles this lane loads
+  const uint32_t c_off = (uint32_t)((cword / NW) * row_bytes + 4 * (cword % NW));
+  uint32_t *cw = reinterpret_cast<uint32_t *>(cring[wave]);  // [4 slots][2 * NW] words
 
   auto load_a = [&](u32x4 (&a)[4], int s) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
-      a[mb] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_off, s * kKS * 2 + mb * a_mb, 0);
+      a[mb] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_off, s * 1024 + mb * a_mb, 0);
   };
-  auto load_c = [&](uint32_t (&c)[8], int s) {
+  auto load_c = [&](uint32_t &c, int s) {
     const long long off = 2LL * s * row_bytes + col_off;
     const __amdgpu_buffer_rsrc_t rc =
         buffer_rsrc(reinterpret_cast<const char *>(P.code) + off, code_bytes - off);
-#pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
-      const int so = ti * (int)row_bytes;
-      c[2 * ti] = __builtin_amdgcn_raw_buffer_load_b32(rc, d0, so, 0);
-      c[2 * ti + 1] = __builtin_amdgcn_raw_buffer_load_b32(rc, d1, so, 0);
-      c[4 + 2 * ti] = __builtin_amdgcn_raw_buffer_load_b32(rc, d0 + NW * 4, so, 0);
-      c[4 + 2 * ti + 1] = __builtin_amdgcn_raw_buffer_load_b32(rc, d1 + NW * 4, so, 0);
-    }
+    c = __builtin_amdgcn_raw_buffer_load_b32(rc, c_off, 0, 0);
   };
-  auto decode_to = [&](const uint32_t (&c)[8], int slot) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const u32x2 t0 = decode_pairs<K>(c[4 * j], c[4 * j + 1], lw.sh);
-      const u32x2 t1 = decode_pairs<K>(c[4 * j + 2], c[4 * j + 3], lw.sh);
-      ring[slot][2 * wave + j][lane] = u32x4{t0[0], t0[1], t1[0], t1[1]};
-    }
+  auto stage_c = [&](uint32_t c, int slot) {
+    cw[slot * 2 * NW + cword] = c;  // repeated lanes store equal data
   };
-  auto mfma_step = [&](const u32x4 (&a)[4], int slot) {
+  auto decode_to = [&](int cslot, int slot) {
+    const uint32_t *w = cw + cslot * 2 * NW;
+    const u32x2 t0 = decode_pairs<K>(w[lw.d0], w[lw.d1], lw.sh);
+    const u32x2 t1 = decode_pairs<K>(w[NW + lw.d0], w[NW + lw.d1], lw.sh);
+    ring[slot][wave][lane] = u32x4{t0[0], t0[1], t1[0], t1[1]};
+  };
+  // B operands of one step: column blocks 0..3 are read from the ring right after the
+  // barrier that publishes the step and 4..7 half a step later, so each group's LDS
+  // latency hides behind 16 MFMAs of the other.
+  u32x4 B[8];
+  auto read_b = [&](int slot, int nb0) {
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const half8 bf = __builtin_bit_cast(half8, ring[slot][nb][lane]);
+    for (int nb = nb0; nb < nb0 + 4; ++nb) B[nb] = ring[slot][nb][lane];
+  };
+  auto mfma_half = [&](const u32x4 (&a)[4], int nb0) {
+#pragma unroll
+    for (int nb = nb0; nb < nb0 + 4; ++nb)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a[mb]), bf, acc[mb][nb], 0, 0, 0);
-    }
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a[mb]),
+                                                             __builtin_bit_cast(half8, B[nb]), acc[mb][nb], 0, 0, 0);
   };
 
 #pragma unroll
@@ -275,33 +379,72 @@ __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][
 
   const int s0 = 2 * k0, s1 = 2 * k1;
   u32x4 A0[4], A1[4];
-  uint32_t C0[8], C1[8];
-  // Step s uses slot (s - s0) & 1, A(s) in A[that slot]; C(s+1) is decoded during step s.
-  // Loads run two steps ahead; past the piece they fetch unused data.
+  uint32_t CR0, CR1;
+  // Step s (relative r = s - s0) uses B ring slot r & 1 and A registers of that parity; its
+  // codes sit in code ring slot r & 3.  During step s the codes of step s+1 are decoded
+  // into the other B slot and the codes of step s+2 are staged; codes and activations
+  // are loaded two steps ahead (past the piece they fetch unused data).
+  // The previous piece's output stores must have completed first: with stores and loads
+  // both outstanding the compiler can no longer count loads in order and would wait for
+  // all of them inside the loop.  The prologue issues its loads in the loop's own order.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  load_c(CR0, s0);
+  __builtin_amdgcn_sched_barrier(0);
   load_a(A0, s0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_c(CR1, s0 + 1);
+  __builtin_amdgcn_sched_barrier(0);
   load_a(A1, s0 + 1);
-  load_c(C0, s0);
-  load_c(C1, s0 + 1);
-  decode_to(C0, 0);
-  load_c(C0, s0 + 2);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_c(CR0, 0);
+  load_c(CR0, s0 + 2);
+  stage_c(CR1, 1);
+  load_c(CR1, s0 + 3);
+  decode_to(0, 0);
   lds_barrier();
-  for (int s = s0; s < s1; s += 2) {
-    decode_to(C1, 1);  // step s + 1
-    load_c(C1, s + 3);
-    mfma_step(A0, 0);  // step s
+  read_b(0, 0);
+  // Before each barrier a wave has 16 MFMAs and one step's decode (about 40 VALU
+  // instructions); they are issued interleaved so that the matrix core and the vector ALU
+  // work at the same time (the two waves of a SIMD reach this point together).
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+    }
+  };
+  for (int s = s0, r = 0; s < s1; s += 2, r += 2) {
+    // step s (B slot 0)
+    mfma_half(A0, 0);
+    read_b(0, 4);
+    stage_c(CR0, (r + 2) & 3);  // codes of step s + 2
+    load_c(CR0, s + 4);
+    decode_to((r + 1) & 3, 1);  // step s + 1
+    interleave();
+    lds_barrier();
+    read_b(1, 0);
+    mfma_half(A0, 4);
     load_a(A0, s + 2);
+    // step s + 1 (B slot 1)
+    mfma_half(A1, 0);
+    read_b(1, 4);
+    stage_c(CR1, (r + 3) & 3);  // codes of step s + 3
+    load_c(CR1, s + 5);
+    decode_to((r + 2) & 3, 0);  // step s + 2 (unused after the last pair)
+    interleave();
     lds_barrier();
-    decode_to(C0, 0);  // step s + 2 (unused after the last pair)
-    load_c(C0, s + 4);
-    mfma_step(A1, 1);  // step s + 1
+    read_b(0, 0);               // step s + 2 (unused after the last pair)
+    mfma_half(A1, 4);
     load_a(A1, s + 3);
-    lds_barrier();
   }
+  lds_barrier();  // the rings' last reads are done before the next piece writes them
 }
 
 template <int K>
-__global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {
-  __shared__ __attribute__((aligned(16))) u32x4 ring[2][8][64];
+__global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  // 2 waves per SIMD
+  __shared__ __attribute__((aligned(16))) u32x4 ring[2][8][64];         // decoded B operands
+  __shared__ __attribute__((aligned(16))) u32x4 cring[kWaves][4 * 2 * 32 / 4];  // staged codes
+  __shared__ uint32_t arrivals;
   const int g = xcd_range(blockIdx.x, P.G);
   long long it = range_start(P, g);
   const long long end = range_start(P, g + 1);
@@ -311,46 +454,31 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {
     const int k0 = (int)(it - (long long)t * P.S);
     const int k1 = (int)min((long long)P.S, (long long)k0 + (end - it));
     Acc acc;
-    run_piece<K>(P, ring, t, k0, k1, acc);
+    run_piece<K>(P, ring, cring, t, k0, k1, acc);
     if (k0 == 0 && k1 == P.S) {
       finish_tile(P, acc, t / P.nNT, t % P.nNT);
     } else {
-      float *dst = partial_ptr(P, 2 * g + (first ? 0 : 1));
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
-          *reinterpret_cast<floatx4 *>(dst + (size_t)(mb * 8 + nb) * 64 * 4) = acc[mb][nb];
+      // Part of a split tile: store it, count the arrival; the last of the tile's
+      // contributors adds all partial tiles (in range order, so the sum does not depend on
+      // which one arrives last) and finishes the tile.  Nobody waits for anybody.
+      store_partial(P, 2 * g + (first ? 0 : 1), acc);
+      __syncthreads();  // every thread's partial stores have completed
+      if (threadIdx.x == 0)
+        arrivals = __hip_atomic_fetch_add(P.counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const long long ts = (long long)t * P.S;
+      const int g0 = range_owner(P, ts), g1 = range_owner(P, ts + P.S - 1);
+      if (arrivals == (uint32_t)(g1 - g0)) {
+        // A contributor's piece of tile t is its first piece (slot 2c) when its range
+        // starts inside t, else its last piece (slot 2c + 1).
+        for (int c = g0; c <= g1; ++c)
+          add_partial(P, 2 * c + (range_start(P, c) >= ts ? 0 : 1), acc, c == g0);
+        finish_tile(P, acc, t / P.nNT, t % P.nNT);
+      }
     }
     it += k1 - k0;
     first = false;
   }
-}
-
-// Workgroup f finishes the tile that its range ends in when that tile is split and f is
-// its first contributor.  A contributor's piece of tile t is its first piece (slot 2c)
-// when its range starts inside t, else its last piece (slot 2c + 1).
-__global__ __launch_bounds__(kThreads) void gemm_fixup_kernel(GemmParams P) {
-  const int f = blockIdx.x;
-  const long long e = range_start(P, f + 1) - 1;
-  const int t = (int)(e / P.S);
-  const long long ts = (long long)t * P.S;
-  const int g0 = range_owner(P, ts), g1 = range_owner(P, ts + P.S - 1);
-  if (g0 == g1 || g0 != f) return;
-  Acc acc;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int c = g0; c <= g1; ++c) {
-    const float *src = partial_ptr(P, 2 * c + (range_start(P, c) >= ts ? 0 : 1));
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
-        acc[mb][nb] += *reinterpret_cast<const floatx4 *>(src + (size_t)(mb * 8 + nb) * 64 * 4);
-  }
-  finish_tile(P, acc, t / P.nNT, t % P.nNT);
 }
 
 int device_cu_count() {
@@ -369,7 +497,7 @@ struct Plan {
   int S, nNT, T, G;
   long long I, q;
   int r;
-  size_t xh_bytes, bytes;
+  size_t xh_bytes, partials_off, counters_off, bytes;
 };
 
 Plan plan(int in_features, int out_features, int M) {
@@ -378,7 +506,7 @@ Plan plan(int in_features, int out_features, int M) {
   p.nNT = out_features / kNT;
   p.T = (M + kMT - 1) / kMT * p.nNT;
   p.I = (long long)p.T * p.S;
-  long long G = 2LL * device_cu_count();  // two workgroups per CU
+  long long G = device_cu_count();  // one workgroup (8 waves) per CU
   const long long by_work = (p.I + kMinSteps - 1) / kMinSteps;
   if (G > by_work) G = by_work;
   // Debug/test override of the workgroup count (exercises many split patterns).
@@ -391,8 +519,10 @@ Plan plan(int in_features, int out_features, int M) {
   p.G = (int)G;
   p.q = p.I / G;
   p.r = (int)(p.I % G);
-  p.xh_bytes = ((size_t)M * in_features * 2 + 255) / 256 * 256;
-  p.bytes = p.xh_bytes + (size_t)2 * p.G * kTileFloats * sizeof(float);
+  p.xh_bytes = (size_t)((M + 15) / 16) * 16 * in_features * 2;  // whole 16-row blocks
+  p.partials_off = p.xh_bytes;
+  p.counters_off = p.partials_off + (size_t)2 * p.G * kTileFloats * sizeof(float);
+  p.bytes = p.counters_off + ((size_t)p.T * 4 + 255) / 256 * 256;
   return p;
 }
 
@@ -410,8 +540,14 @@ hipError_t launch_gemm(const trellis_linear &L, const uint16_t *x, int M, uint16
   if (ws_bytes < p.bytes) return hipErrorInvalidValue;
   if (p.G > (1 << 20)) return hipErrorInvalidValue;
   uint16_t *xh = static_cast<uint16_t *>(ws);
-  const long long tasks = (long long)M * (L.in_features / 128);
-  rotate_kernel<<<(unsigned)((tasks + 3) / 4), 256, 0, stream>>>(x, M, L.in_features, L.rin, L.s_in, xh);
+  uint32_t *counters = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + p.counters_off);
+  if ((long long)(M + 15) / 16 * (L.in_features / 128) >= (1LL << 31)) return hipErrorInvalidValue;
+  const unsigned rgrid = (unsigned)((M + 15) / 16 * (L.in_features / 128));
+  const bool vec = (reinterpret_cast<uintptr_t>(L.rin) % 16) == 0 && (reinterpret_cast<uintptr_t>(L.s_in) % 16) == 0;
+  if (vec)
+    rotate_kernel<true><<<rgrid, 256, 0, stream>>>(x, M, L.in_features, L.rin, L.s_in, xh, counters, p.T);
+  else
+    rotate_kernel<false><<<rgrid, 256, 0, stream>>>(x, M, L.in_features, L.rin, L.s_in, xh, counters, p.T);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   GemmParams P;
@@ -420,7 +556,8 @@ hipError_t launch_gemm(const trellis_linear &L, const uint16_t *x, int M, uint16
   P.rout = L.rout;
   P.s_out = L.s_out;
   P.y = y;
-  P.partials = reinterpret_cast<float *>(static_cast<char *>(ws) + p.xh_bytes);
+  P.partials = reinterpret_cast<float *>(static_cast<char *>(ws) + p.partials_off);
+  P.counters = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + p.counters_off);
   P.M = M;
   P.in = L.in_features;
   P.out = L.out_features;
@@ -435,9 +572,6 @@ hipError_t launch_gemm(const trellis_linear &L, const uint16_t *x, int M, uint16
     case 4: gemm_sk_kernel<4><<<p.G, kThreads, 0, stream>>>(P); break;
     default: return hipErrorInvalidValue;
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  gemm_fixup_kernel<<<p.G, kThreads, 0, stream>>>(P);
   return hipGetLastError();
 }
 
