@@ -2,32 +2,39 @@
 //
 // ("Escha-W2 runs on Metal", reconstruction paragraph; decode as in decode.hip.)
 //
-// Three launches:
+// Two launches:
 //   1. rotate: XH = H128(X*su) (unnormalised butterfly) as fp16 in the workspace, stored in
 //      1 KB blocks of 16 rows x one k-step laid out exactly as the MFMA A operands are held
-//      by the lanes, so every A-operand load is one contiguous 1 KB piece;
-//   2. the stream-K product.  Output tiles are 256 rows x 128 columns (one Hadamard block)
-//      and a tile's k-steps are 32 input rows (two trellis tile rows).  The (tile, k-step)
-//      iterations are numbered tile-major and every workgroup takes one contiguous range
-//      of them, so all workgroups do the same work whatever the tile count; consecutive
-//      ranges go to the same XCD (the dispatcher deals workgroups round-robin over the
-//      XCDs), so an XCD works on one band of rows and keeps its activations in its L2.
-//      A workgroup is 4 waves; wave w owns output rows 64w..64w+63 of the tile (4 x 8
+//      by the lanes, so every A-operand load is one contiguous, fully used 1 KB piece.  It
+//      also clears the split-tile counters.
+//   2. the stream-K product.  Output tiles are 512 rows x 128 columns (one Hadamard block)
+//      and a tile's k-steps are 32 input rows (two trellis tile rows), taken in pairs.  The
+//      (tile, k-step pair) iterations are numbered tile-major and each of the G workgroups
+//      (one per CU) takes one contiguous range of them, so every workgroup does the same
+//      work whatever the tile count; consecutive ranges go to the same XCD (the dispatcher
+//      deals workgroups round-robin over the XCDs).
+//
+//      A workgroup is 8 waves; wave w owns output rows 64w..64w+63 of the tile (4 x 8
 //      blocks of 16x16, fp32 accumulators) and, per k-step, decodes the two trellis tile
-//      rows of column blocks 2w and 2w+1 directly into MFMA B operands: by the lane
-//      assignment of the decoder a lane's four symbols of a tile sit in one tile column and
-//      four tile rows, so the lane holds, for its column, eight weights along k -- exactly
-//      one B operand of v_mfma_f32_16x16x32_f16 once k inside the step is numbered as the
-//      lanes hold it.  The operands go through a two-slot LDS ring (1 KB per column block)
-//      so all four waves use all eight column blocks.  Codes and activations are loaded
-//      two k-steps ahead into registers.  The codebook's fp16 addition (one rounding)
-//      happens in the decoder, so B holds the format's exact fp16 weights.
+//      rows of column block w directly into one MFMA B operand: by the lane assignment of
+//      the decoder a lane's four symbols of a tile sit in one tile column and four tile
+//      rows, so the lane holds, for its column, eight weights along k -- exactly one B
+//      operand of v_mfma_f32_16x16x32_f16 once k inside the step is numbered as the lanes
+//      hold it.  The operands go through a two-slot LDS ring (1 KB per column block) so all
+//      waves use all eight column blocks; half of them are read right after the barrier
+//      that publishes a step and half a step later, behind 16 MFMAs.  Codes (one 4-byte
+//      word per lane covers a step's two tiles) go through a wave-private LDS ring; codes
+//      and activations are loaded two k-steps ahead into registers.  The codebook's fp16
+//      addition (one rounding) happens in the decoder, so B holds the format's exact fp16
+//      weights.
+//
 //      A range covering a whole tile finishes it: output Hadamard across the tile's 128
 //      columns (16 lanes x 8 registers per row), scales, the exact 1/128, fp16 stores.
-//      The first or last piece of a range that covers only part of a tile is stored as an
-//      fp32 partial tile in the workspace instead;
-//   3. fix-up: one workgroup per split tile adds its partial tiles in range order
-//      (deterministic) and finishes the tile as above.
+//      A tile split between two ranges: the first contributor to arrive stores its fp32
+//      partial tile; the second adds it to its registers and finishes the tile.  Tiles
+//      split among three or more (short ranges): every contributor stores, the last to
+//      arrive adds all partials in range order.  Nobody waits for a workgroup that has not
+//      arrived.
 #include <cstdlib>
 
 #include "launch.h"
@@ -52,7 +59,7 @@ struct GemmParams {
   const float *s_out;
   uint16_t *y;
   float *partials;     // [2G][kTileFloats]
-  uint32_t *counters;  // [T] arrivals per tile, zeroed by the rotation launch
+  uint32_t *counters;  // [T][2] (arrived, stored) per tile, zeroed by the rotation launch
   int M, in, out;
   int S;               // k-step pairs per tile (the unit of the ranges)
   int nNT;             // column tiles
@@ -303,7 +310,8 @@ __device__ __forceinline__ void add_partial(const GemmParams &P, int slot, Acc &
 // Accumulates k-step pairs [k0, k1) of tile t (k-steps 2*k0 .. 2*k1 - 1).
 template <int K>
 __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][64],
-                                          u32x4 (*cring)[4 * 2 * 32 / 4], int t, int k0, int k1, Acc &acc) {
+                                          u32x4 (*cring)[4 * 2 * 32 / 4], int t, int k0, int k1, Acc &acc,
+                                          int signal) {
   constexpr int NW = 8 * K;  // 32-bit words per trellis tile
   // The lane's constants are recomputed per piece rather than kept live across the
   // epilogue (where they would be spilled and reloaded just before the loop, and the wait
@@ -402,6 +410,10 @@ __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][
   load_c(CR1, s0 + 3);
   decode_to(0, 0);
   lds_barrier();
+  // Every thread passed vmcnt(0) above, so partial-tile stores issued before this piece
+  // have completed: publish them now (their latency was hidden behind the prologue).
+  if (signal >= 0 && threadIdx.x == 0)
+    __hip_atomic_fetch_add(P.counters + 2 * signal + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   read_b(0, 0);
   // Before each barrier a wave has 16 MFMAs and one step's decode (about 40 VALU
   // instructions); they are issued interleaved so that the matrix core and the vector ALU
@@ -449,35 +461,69 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
   long long it = range_start(P, g);
   const long long end = range_start(P, g + 1);
   bool first = true;
+  int signal = -1;  // split tile whose stored partial is still to be published
   while (it < end) {
     const int t = (int)(it / P.S);
     const int k0 = (int)(it - (long long)t * P.S);
     const int k1 = (int)min((long long)P.S, (long long)k0 + (end - it));
     Acc acc;
-    run_piece<K>(P, ring, cring, t, k0, k1, acc);
+    run_piece<K>(P, ring, cring, t, k0, k1, acc, signal);
+    signal = -1;
     if (k0 == 0 && k1 == P.S) {
       finish_tile(P, acc, t / P.nNT, t % P.nNT);
     } else {
-      // Part of a split tile: store it, count the arrival; the last of the tile's
-      // contributors adds all partial tiles (in range order, so the sum does not depend on
-      // which one arrives last) and finishes the tile.  Nobody waits for anybody.
-      store_partial(P, 2 * g + (first ? 0 : 1), acc);
-      __syncthreads();  // every thread's partial stores have completed
-      if (threadIdx.x == 0)
-        arrivals = __hip_atomic_fetch_add(P.counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
       const long long ts = (long long)t * P.S;
       const int g0 = range_owner(P, ts), g1 = range_owner(P, ts + P.S - 1);
-      if (arrivals == (uint32_t)(g1 - g0)) {
-        // A contributor's piece of tile t is its first piece (slot 2c) when its range
-        // starts inside t, else its last piece (slot 2c + 1).
-        for (int c = g0; c <= g1; ++c)
-          add_partial(P, 2 * c + (range_start(P, c) >= ts ? 0 : 1), acc, c == g0);
-        finish_tile(P, acc, t / P.nNT, t % P.nNT);
+      const int own = 2 * g + (first ? 0 : 1);
+      if (g1 == g0 + 1) {
+        // Two contributors.  Counters (arrived, stored) per tile.  The first to arrive
+        // stores its partial tile and publishes it later (start of its next piece, or
+        // its end); the second adds that partial to its own registers (two terms: the
+        // sum does not depend on the order) and finishes the tile.  The second only
+        // waits for a contributor that has already arrived, i.e. is running.
+        if (threadIdx.x == 0)
+          arrivals = __hip_atomic_fetch_add(P.counters + 2 * t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (arrivals == 0) {
+          store_partial(P, own, acc);
+          signal = t;
+        } else {
+          if (threadIdx.x == 0) {
+            for (int spin = 0; spin < (1 << 24); ++spin) {
+              if (__hip_atomic_load(P.counters + 2 * t + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+              __builtin_amdgcn_s_sleep(2);
+            }
+          }
+          __syncthreads();
+          const int c = g0 + g1 - g;  // the other contributor
+          add_partial(P, 2 * c + (range_start(P, c) >= ts ? 0 : 1), acc, false);
+          finish_tile(P, acc, t / P.nNT, t % P.nNT);
+        }
+      } else {
+        // Three or more contributors (ranges shorter than a tile): every one stores its
+        // partial tile; the last to arrive adds all of them in range order, so the sum
+        // does not depend on which one arrives last.
+        store_partial(P, own, acc);
+        __syncthreads();  // every thread's partial stores have completed
+        if (threadIdx.x == 0)
+          arrivals = __hip_atomic_fetch_add(P.counters + 2 * t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (arrivals == (uint32_t)(g1 - g0)) {
+          // A contributor's piece of tile t is its first piece (slot 2c) when its range
+          // starts inside t, else its last piece (slot 2c + 1).
+          for (int c = g0; c <= g1; ++c)
+            add_partial(P, 2 * c + (range_start(P, c) >= ts ? 0 : 1), acc, c == g0);
+          finish_tile(P, acc, t / P.nNT, t % P.nNT);
+        }
       }
     }
     it += k1 - k0;
     first = false;
+  }
+  if (signal >= 0) {
+    __syncthreads();  // the stores of the last piece's partial have completed
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(P.counters + 2 * signal + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -522,7 +568,7 @@ Plan plan(int in_features, int out_features, int M) {
   p.xh_bytes = (size_t)((M + 15) / 16) * 16 * in_features * 2;  // whole 16-row blocks
   p.partials_off = p.xh_bytes;
   p.counters_off = p.partials_off + (size_t)2 * p.G * kTileFloats * sizeof(float);
-  p.bytes = p.counters_off + ((size_t)p.T * 4 + 255) / 256 * 256;
+  p.bytes = p.counters_off + ((size_t)p.T * 8 + 255) / 256 * 256;
   return p;
 }
 
@@ -545,9 +591,9 @@ hipError_t launch_gemm(const trellis_linear &L, const uint16_t *x, int M, uint16
   const unsigned rgrid = (unsigned)((M + 15) / 16 * (L.in_features / 128));
   const bool vec = (reinterpret_cast<uintptr_t>(L.rin) % 16) == 0 && (reinterpret_cast<uintptr_t>(L.s_in) % 16) == 0;
   if (vec)
-    rotate_kernel<true><<<rgrid, 256, 0, stream>>>(x, M, L.in_features, L.rin, L.s_in, xh, counters, p.T);
+    rotate_kernel<true><<<rgrid, 256, 0, stream>>>(x, M, L.in_features, L.rin, L.s_in, xh, counters, 2 * p.T);
   else
-    rotate_kernel<false><<<rgrid, 256, 0, stream>>>(x, M, L.in_features, L.rin, L.s_in, xh, counters, p.T);
+    rotate_kernel<false><<<rgrid, 256, 0, stream>>>(x, M, L.in_features, L.rin, L.s_in, xh, counters, 2 * p.T);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   GemmParams P;
