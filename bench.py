@@ -203,10 +203,10 @@ def run_prefill(args, torch, tb, synth):
     L = tb.TrellisLinear.from_host(lin)
     x = torch.from_numpy(wl.xs["w"]).cuda()
     y = torch.empty((x.shape[0], lin.out_features), dtype=torch.float16, device="cuda")
-    for _ in range(max(2, args.warmup)):
+    for _ in range(max(10, args.warmup)):  # also lets the clocks settle under the MFMA load
         tb.trellis_gemm(L, x, out=y)
     torch.cuda.synchronize()
-    n = max(5, args.steps // 4)
+    n = max(10, args.steps // 2)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(n):
