@@ -83,6 +83,22 @@ def test_gemv_dense_mlp_full_size(which):
     assert rel_l2(got, ref) < REL_L2_TOL
 
 
+def test_dense_mlp_gate_up_as_one_launch():
+    """The dense step's gate (K2) and up (K3) share x and run as one launch over a 2-entry
+    table: each output row must match the oracle (sampled column blocks)."""
+    log_case("gate+up one launch")
+    wl = synth.dense_mlp(0)
+    gate, up, x = wl.layers["gate"], wl.layers["up"], wl.xs["gate"]
+    table = tb.ExpertTable([dev_linear(gate), dev_linear(up)])
+    routed = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    y = tb.trellis_moe_gemv(table, routed, to_dev(x[0]), False).cpu().numpy()
+    blocks = [0, 77, 135]
+    for row, lin in enumerate([gate, up]):
+        ref = O.forward_linear(lin, x, col_blocks=blocks)
+        got = np.concatenate([y[row:row + 1, 128 * J:128 * J + 128] for J in blocks], axis=1)
+        assert rel_l2(got, ref) < REL_L2_TOL, row
+
+
 def test_gemv_shape_changes_share_workspace():
     """Calls of different shapes back to back on one workspace (the counters of a wide call
     must not be disturbed by the partial sums of an earlier narrow one)."""
