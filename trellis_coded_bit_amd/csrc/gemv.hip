@@ -252,7 +252,8 @@ __device__ __forceinline__ void dma_unit(const uint32_t *row0, size_t row_stride
 // sub-range issues its rotation loads and its first code copies, rotates while the code is
 // in flight, then streams with SLOTS - 1 units in flight per wave.
 template <int K>
-__device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &pr, int p, int ub, int ue) {
+__device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &pr, int p, int ub, int ue,
+                            bool fresh) {
   using RG = Ring<K>;
   constexpr int NW = RG::NW;
   constexpr int SLOTS = RG::SLOTS;
@@ -283,6 +284,20 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
     int cur_I = __builtin_amdgcn_readfirstlane((first + sb) % nI);
     int cur_J = __builtin_amdgcn_readfirstlane((first + sb) / nI);
     int pre_I = cur_I, pre_J = cur_J;
+    // the previous sub-range's reads of the A buffer and of the ring are finished (nothing
+    // to wait for on the workgroup's first sub-range)
+    if (!(fresh && sb == 0)) __syncthreads();
+    // The first unit into slot 0, then the rotation's loads; units 1..SLOTS-2 are requested
+    // after the rotation.  At the start of the kernel every wave requests code at once: asking for
+    // one unit each first lets the memory system serve everybody's first unit before the
+    // deeper prefetches, so the decode starts sooner.
+    auto prime = [&](int j) {
+      const bool real = j < n;
+      dma_unit<K>(code + (size_t)pre_I * row_block_words + (size_t)(8 * pre_J) * NW, row_stride,
+                  ring + j * (RG::UNIT_BYTES / 4), real);
+      if (real && ++pre_I == nI) { pre_I = 0; ++pre_J; }
+    };
+    prime(0);
     RotLoads rq;
 #pragma unroll
     for (int t = 0; t < kMaxTasks; ++t) {
@@ -299,18 +314,10 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
         rq.s1[t] = pr.s_in ? ldg(pr.s_in + k1) : 1.f;
       }
     }
-    // the previous sub-range's reads of the A buffer and of the ring are finished
-    __syncthreads();
-    // first SLOTS-1 units into slots 0..SLOTS-2
-#pragma unroll
-    for (int j = 0; j < SLOTS - 1; ++j) {
-      const bool real = j < n;
-      dma_unit<K>(code + (size_t)pre_I * row_block_words + (size_t)(8 * pre_J) * NW, row_stride,
-                  ring + j * (RG::UNIT_BYTES / 4), real);
-      if (real && ++pre_I == nI) { pre_I = 0; ++pre_J; }
-    }
     rotation_compute(B, n, wave, rq, sm);
-    __syncthreads();
+    __syncthreads();  // (also waits for unit 0)
+#pragma unroll
+    for (int j = 1; j < SLOTS - 1; ++j) prime(j);
 
     int slot = 0;
     for (int k = 0; k < n; ++k) {
@@ -362,20 +369,28 @@ __device__ void run_invalid(const GemvParams &P, const Lds &sm, int ub, int ue) 
   }
 }
 
+// KS = 2, 3, 4: one layer of that width (no table, the K dispatch compiled away, a smaller
+// kernel); KS = 0: a list of problems with per-entry K.
+template <int KS>
 __global__ __launch_bounds__(kThreads, 4) void gemv_partial_kernel(GemvParams P) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   const Lds sm = lds_carve(lds_raw, P.L.B, P.kA);
   const int g = blockIdx.x;
   const int u0 = wg_start(g, P.U, P.G), u1 = wg_start(g + 1, P.U, P.G);
+  if constexpr (KS != 0) {
+    if (u0 < u1) run_problem<KS>(P, sm, get_problem(P, 0), 0, u0, u1, true);
+    return;
+  }
   const int per_problem = P.nI * P.nJ;
   for (int u = u0; u < u1;) {
     const int p = u / per_problem;
     const int ue = min(u1, (p + 1) * per_problem);
     const Problem pr = get_problem(P, p);
+    const bool fresh = u == u0;
     switch (pr.ok ? pr.K : 0) {
-      case 2: run_problem<2>(P, sm, pr, p, u, ue); break;
-      case 3: run_problem<3>(P, sm, pr, p, u, ue); break;
-      case 4: run_problem<4>(P, sm, pr, p, u, ue); break;
+      case 2: run_problem<2>(P, sm, pr, p, u, ue, fresh); break;
+      case 3: run_problem<3>(P, sm, pr, p, u, ue, fresh); break;
+      case 4: run_problem<4>(P, sm, pr, p, u, ue, fresh); break;
       default: run_invalid(P, sm, u, ue); break;
     }
     u = ue;
@@ -463,7 +478,7 @@ int device_cus_and_occupancy(int B, int *cus_out) {
   }
   if (d.occ[B] == 0) {
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_partial_kernel, kThreads,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_partial_kernel<0>, kThreads,
                                                      lds_bytes(B, kWaves * kMaxTasks / B)) != hipSuccess ||
         occ <= 0)
       occ = 2;
@@ -536,7 +551,11 @@ hipError_t launch_gemv(const GemvLaunch &a, void *ws, size_t ws_bytes, hipStream
   P.nJ = gm.nJ;
   P.maxseg = gm.maxseg;
   P.kA = gm.kA;
-  gemv_partial_kernel<<<gm.G, kThreads, lds_bytes(a.B, gm.kA), stream>>>(P);
+  const size_t lds = lds_bytes(a.B, gm.kA);
+  if (a.table == nullptr && a.single.K == 2) gemv_partial_kernel<2><<<gm.G, kThreads, lds, stream>>>(P);
+  else if (a.table == nullptr && a.single.K == 3) gemv_partial_kernel<3><<<gm.G, kThreads, lds, stream>>>(P);
+  else if (a.table == nullptr && a.single.K == 4) gemv_partial_kernel<4><<<gm.G, kThreads, lds, stream>>>(P);
+  else gemv_partial_kernel<0><<<gm.G, kThreads, lds, stream>>>(P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   gemv_finish_kernel<<<gm.nq, kThreads, 0, stream>>>(P);
