@@ -86,10 +86,12 @@ struct Problem {
   bool ok;
 };
 
+// TABLE = false: the launch is known to be a single layer (no table lookups at all).
+template <bool TABLE = true>
 __device__ __forceinline__ Problem get_problem(const GemvParams &P, int p) {
   trellis_linear d = P.L.single;
   bool ok = true;
-  if (P.L.table) {
+  if (TABLE && P.L.table) {
     const int e = P.L.routed[p];
     if (e < 0 || e >= P.L.E) ok = false;
     else d = P.L.table[e];
@@ -113,9 +115,12 @@ __device__ __forceinline__ Problem get_problem(const GemvParams &P, int p) {
 }
 
 // First unit of workgroup g, and the workgroup owning unit u (largest g with start(g) <= u).
-__host__ __device__ __forceinline__ int wg_start(int g, int U, int G) { return (int)(((long long)g * U) / G); }
+// 32-bit arithmetic: the launch checks G * U < 2^32.
+__host__ __device__ __forceinline__ int wg_start(int g, int U, int G) {
+  return (int)(((unsigned)g * (unsigned)U) / (unsigned)G);
+}
 __host__ __device__ __forceinline__ int owner(int u, int U, int G) {
-  return (int)((((long long)u + 1) * G - 1) / U);
+  return (int)(((unsigned)(u + 1) * (unsigned)G - 1u) / (unsigned)U);
 }
 
 // Orders this wave's LDS accesses (all lanes of one wave run in lockstep and the LDS
@@ -378,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_partial_kernel(GemvParams P)
   const int g = blockIdx.x;
   const int u0 = wg_start(g, P.U, P.G), u1 = wg_start(g + 1, P.U, P.G);
   if constexpr (KS != 0) {
-    if (u0 < u1) run_problem<KS>(P, sm, get_problem(P, 0), 0, u0, u1, true);
+    if (u0 < u1) run_problem<KS>(P, sm, get_problem<false>(P, 0), 0, u0, u1, true);
     return;
   }
   const int per_problem = P.nI * P.nJ;
@@ -407,6 +412,16 @@ __global__ __launch_bounds__(kThreads) void gemv_finish_kernel(GemvParams P) {
   const int B = P.L.B, out = P.L.out_features;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = blockIdx.x;
+  // the output-side vectors are requested first (their loads overlap the partials')
+  const int p = q / P.nJ, J = q - p * P.nJ;
+  const Problem pr = get_problem(P, p);
+  const int c0 = J * 128 + lane, c1 = c0 + 64;
+  float sa = 0.f, sb = 0.f;
+  if (pr.ok) {
+    sa = h2f(ldg(pr.rout + c0)) * (1.0f / 128.0f);
+    sb = h2f(ldg(pr.rout + c1)) * (1.0f / 128.0f);
+    if (pr.s_out) { sa *= ldg(pr.s_out + c0); sb *= ldg(pr.s_out + c1); }
+  }
   const int g_lo = owner(q * P.nI, P.U, P.G), g_hi = owner((q + 1) * P.nI - 1, P.U, P.G);
   float v[kMaxB * 128 / kThreads];
 #pragma unroll
@@ -416,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void gemv_finish_kernel(GemvParams P) {
     __syncthreads();
     if (tid < kPartialBatch) {
       const int gg = gb + tid;
-      slot_of[tid] = gg <= g_hi ? gg * P.maxseg + (q - (int)((unsigned)(gg * P.U) / (unsigned)P.G) / P.nI) : -1;
+      slot_of[tid] = gg <= g_hi ? gg * P.maxseg + (q - (int)(((unsigned)gg * (unsigned)P.U) / (unsigned)P.G) / P.nI) : -1;
     }
     __syncthreads();
 #pragma unroll
@@ -440,16 +455,11 @@ __global__ __launch_bounds__(kThreads) void gemv_finish_kernel(GemvParams P) {
     if (idx < B * 128) fin[idx >> 7][idx & 127] = v[i];
   }
   __syncthreads();
-  const int p = q / P.nJ, J = q - p * P.nJ;
-  const Problem pr = get_problem(P, p);
   uint16_t *y = P.L.y + (size_t)p * B * out;
   for (int b = wave; b < B; b += kWaves) {
-    const int c0 = J * 128 + lane, c1 = c0 + 64;
     float va = fin[b][lane], vb = fin[b][lane + 64];
     if (pr.ok) {
       wave_fwht128(va, vb);
-      float sa = h2f(ldg(pr.rout + c0)) * (1.0f / 128.0f), sb = h2f(ldg(pr.rout + c1)) * (1.0f / 128.0f);
-      if (pr.s_out) { sa *= ldg(pr.s_out + c0); sb *= ldg(pr.s_out + c1); }
       va *= sa;
       vb *= sb;
     } else {
