@@ -283,6 +283,8 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
   floatx4 acc[8];
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int wg_u1 = __builtin_amdgcn_readfirstlane(wg_start(blockIdx.x + 1, P.U, P.G));
+  const int wg_units = __builtin_amdgcn_readfirstlane(wg_u1 - wg_start(blockIdx.x, P.U, P.G));
 
   for (int sb = 0; sb < total; sb += P.kA) {
     const int n = __builtin_amdgcn_readfirstlane(min(P.kA, total - sb));
@@ -335,6 +337,18 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
         if (real && ++pre_I == nI) { pre_I = 0; ++pre_J; }
       }
       wait_vmcnt<RG::WAIT>();  // unit k has landed
+      {
+        // Issue priority from the share of the range still to do (quarters; 3 = most left).
+        // The waves of a CU otherwise issue oldest-first, so the workgroups resident on a
+        // CU would finish one after another and the last would run with few waves at the
+        // end; with this rule the ones behind catch up and they finish together.
+        const int left = wg_u1 - (ub + sb + k);
+        const int prio = (left * 4 - 1) / wg_units;
+        if (prio >= 3) __builtin_amdgcn_s_setprio(3);
+        else if (prio == 2) __builtin_amdgcn_s_setprio(2);
+        else if (prio == 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
       const uint32_t *ub_ = ring + slot * (RG::UNIT_BYTES / 4);
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
@@ -404,7 +418,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_partial_kernel(GemvParams P)
 
 // One workgroup per column block q: sum the contributors' partials in workgroup order,
 // rotate, scale and write fp16 y.
-constexpr int kPartialBatch = 16;  // partial loads a thread issues together
+constexpr int kPartialBatch = 32;  // partial loads a thread issues together
 
 __global__ __launch_bounds__(kThreads) void gemv_finish_kernel(GemvParams P) {
   __shared__ float fin[kMaxB][128];
