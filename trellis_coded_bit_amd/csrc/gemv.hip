@@ -14,11 +14,12 @@
 //    Each workgroup writes one fp32 partial sum y_pre[B][128] per column block it touches
 //    (its "segment") into the workspace.  Inside a workgroup (4 waves) every wave takes
 //    two of the unit's eight tile rows:
-//      * loads: the wave's 2 x 8 tiles are 2 x 256K contiguous bytes; each lane loads
-//        8-byte pieces (fully coalesced) kPrefetch units ahead of use, into a ring of
-//        registers, and stages them in a wave-private LDS buffer; each tile is stored with
-//        a copy of its last word in front, so a lane's circular window is two adjacent
-//        LDS words;
+//      * loads: the wave's 2 x 8 tiles are 2 x 256K contiguous bytes, copied straight
+//        from global memory into a wave-private LDS ring (global_load_lds, 16 B per lane,
+//        fully coalesced) several units ahead of use; a lane's circular window is read as
+//        two LDS words of its tile;
+//      * balance: the workgroups resident on one CU set their issue priority from the
+//        share of their range still to do, so they finish together;
 //      * input rotation: per sub-range the workgroup butterflies x*su (unnormalised) and
 //        stores fp16 MFMA A-operands in LDS, each value twice (below);
 //      * contraction: per tile each lane decodes its four symbols (trellis_device.h) to
@@ -46,6 +47,10 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxB = 8;
 constexpr int kMaxTasks = 4;     // (unit, batch row) rotations per wave and sub-range
 constexpr int kABudget = 32768;  // LDS bytes for A operands
+// Code ring per wave.  7 KB keeps a workgroup at batch 1 within 40 KB of LDS, so four
+// workgroups (16 waves) share a CU; more waves per SIMD hide the decode's latencies better
+// than deeper rings hide memory latency (measured).
+constexpr int kRingBytes = 7168;
 
 struct GemvParams {
   GemvLaunch L;
@@ -65,7 +70,7 @@ struct Lds {
 };
 
 __host__ __device__ constexpr size_t lds_a_bytes(int B, int kA) { return (size_t)kA * 8 * 4 * B * 16; }
-__host__ __device__ constexpr size_t lds_tiles_bytes() { return (size_t)kWaves * 8192; }
+__host__ __device__ constexpr size_t lds_tiles_bytes() { return (size_t)kWaves * kRingBytes; }
 __host__ __device__ constexpr size_t lds_bytes(int B, int kA) {
   return lds_a_bytes(B, kA) + lds_tiles_bytes() + (size_t)kWaves * B * 128 * 4;
 }
@@ -200,13 +205,12 @@ __device__ __forceinline__ void publish_partial(const GemvParams &P, const Lds &
 // issuing exactly kDma copies per unit on every path (dummy copies past the end) so that N
 // is a compile-time constant.  Vector memory operations complete in issue order.
 // ---------------------------------------------------------------------------------------
-constexpr int kRingBytes = 8192;
 
 template <int K>
 struct Ring {
   static constexpr int NW = 8 * K;                      // words per tile
   static constexpr int UNIT_BYTES = 16 * NW * 4;       // 1024 / 1536 / 2048
-  static constexpr int SLOTS = kRingBytes / UNIT_BYTES; // 8 / 5 / 4
+  static constexpr int SLOTS = kRingBytes / UNIT_BYTES; // 7 / 4 / 3
   static constexpr int DMA = (K == 2) ? 1 : 2;          // copies per unit
   static constexpr int WAIT = DMA * (SLOTS - 1);        // copies younger than the unit in use
   static_assert(WAIT < 64, "vmcnt range");
