@@ -136,6 +136,14 @@ __device__ __forceinline__ void wave_sync() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Wave issue priority (s_setprio takes an immediate).
+__device__ __forceinline__ void set_priority(int prio) {
+  if (prio >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (prio == 2) __builtin_amdgcn_s_setprio(2);
+  else if (prio == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // ---------------------------------------------------------------------------------------
 // Input rotation.  a[((s*8 + ti)*4 + g)*B + m] holds, for tile row ti of unit s and batch
 // row m, the four words for rows (2g, 2g+1, 2g+8, 2g+9), each word the fp16 value twice.
@@ -287,14 +295,34 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
   floatx4 acc[8];
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // Issue priority from the share of the workgroup's range still to do, in quarters (3 =
+  // more than three quarters left).  The waves of a CU otherwise issue oldest-first, so the
+  // workgroups resident on a CU would finish one after another and the last would run with
+  // few waves at the end; with this rule the ones behind catch up and they finish together.
+  // Priority p applies from unit t[p] = u1 - floor((p + 1) * units / 4) on.
   const int wg_u1 = __builtin_amdgcn_readfirstlane(wg_start(blockIdx.x + 1, P.U, P.G));
   const int wg_units = __builtin_amdgcn_readfirstlane(wg_u1 - wg_start(blockIdx.x, P.U, P.G));
+  const int t2 = wg_u1 - (3 * wg_units) / 4, t1 = wg_u1 - (2 * wg_units) / 4, t0 = wg_u1 - wg_units / 4;
+  auto prio_at = [&](int c) { return c >= t0 ? 0 : c >= t1 ? 1 : c >= t2 ? 2 : 3; };
+  set_priority(prio_at(ub));
 
   for (int sb = 0; sb < total; sb += P.kA) {
     const int n = __builtin_amdgcn_readfirstlane(min(P.kA, total - sb));
     int cur_I = __builtin_amdgcn_readfirstlane((first + sb) % nI);
     int cur_J = __builtin_amdgcn_readfirstlane((first + sb) / nI);
-    int pre_I = cur_I, pre_J = cur_J;
+    int pre_I = cur_I;
+    // next unit to request: its rows start at nxt (uniform); one step along I adds a row
+    // block, the wrap to the next column block moves 8 tiles right and back to I = 0
+    const uint32_t *nxt = code + (size_t)pre_I * row_block_words + (size_t)(8 * cur_J) * NW;
+    const size_t wrap_back = (size_t)(nI - 1) * row_block_words;
+    auto advance = [&]() {
+      if (++pre_I == nI) {
+        pre_I = 0;
+        nxt = nxt - wrap_back + 8 * NW;
+      } else {
+        nxt += row_block_words;
+      }
+    };
     // the previous sub-range's reads of the A buffer and of the ring are finished (nothing
     // to wait for on the workgroup's first sub-range)
     if (!(fresh && sb == 0)) __syncthreads();
@@ -304,9 +332,8 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
     // deeper prefetches, so the decode starts sooner.
     auto prime = [&](int j) {
       const bool real = j < n;
-      dma_unit<K>(code + (size_t)pre_I * row_block_words + (size_t)(8 * pre_J) * NW, row_stride,
-                  ring + j * (RG::UNIT_BYTES / 4), real);
-      if (real && ++pre_I == nI) { pre_I = 0; ++pre_J; }
+      dma_unit<K>(real ? nxt : code, row_stride, ring + j * (RG::UNIT_BYTES / 4), real);
+      if (real) advance();
     };
     prime(0);
     RotLoads rq;
@@ -336,22 +363,13 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
       {
         const int ws = (slot == 0 ? SLOTS : slot) - 1;
         const bool real = k + SLOTS - 1 < n;
-        const uint32_t *row0 = real ? code + (size_t)pre_I * row_block_words + (size_t)(8 * pre_J) * NW : code;
-        dma_unit<K>(row0, row_stride, ring + ws * (RG::UNIT_BYTES / 4), real);
-        if (real && ++pre_I == nI) { pre_I = 0; ++pre_J; }
+        dma_unit<K>(real ? nxt : code, row_stride, ring + ws * (RG::UNIT_BYTES / 4), real);
+        if (real) advance();
       }
       wait_vmcnt<RG::WAIT>();  // unit k has landed
       {
-        // Issue priority from the share of the range still to do (quarters; 3 = most left).
-        // The waves of a CU otherwise issue oldest-first, so the workgroups resident on a
-        // CU would finish one after another and the last would run with few waves at the
-        // end; with this rule the ones behind catch up and they finish together.
-        const int left = wg_u1 - (ub + sb + k);
-        const int prio = (left * 4 - 1) / wg_units;
-        if (prio >= 3) __builtin_amdgcn_s_setprio(3);
-        else if (prio == 2) __builtin_amdgcn_s_setprio(2);
-        else if (prio == 1) __builtin_amdgcn_s_setprio(1);
-        else __builtin_amdgcn_s_setprio(0);
+        const int c = ub + sb + k;
+        if (c == t2 || c == t1 || c == t0) set_priority(prio_at(c));
       }
       const uint32_t *ub_ = ring + slot * (RG::UNIT_BYTES / 4);
 #pragma unroll
