@@ -34,6 +34,7 @@
 //    order (deterministic), applies the output Hadamard, the scales and the exact 1/128
 //    that replaces the two 1/sqrt(128) factors, and writes fp16 y.
 #include <cstdlib>
+#include <type_traits>
 
 #include "launch.h"
 #include "trellis_device.h"
@@ -336,11 +337,13 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
       if (real) advance();
     };
     prime(0);
+    // Rotation loads: straight-line code (tasks past the last are clamped to it and their
+    // values ignored), so all of them are in flight together.
     RotLoads rq;
+    auto load_tasks = [&](auto with_s) {
 #pragma unroll
-    for (int t = 0; t < kMaxTasks; ++t) {
-      const int task = wave + kWaves * t;
-      if (task < n * B) {
+      for (int t = 0; t < kMaxTasks; ++t) {
+        const int task = min(wave + kWaves * t, n * B - 1);
         const int s = task / B, b = task - s * B;
         const int I = (first + sb + s) % nI;
         const int k0 = I * 128 + lane, k1 = k0 + 64;
@@ -348,10 +351,17 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
         rq.x1[t] = h2f(ldg(xp + (size_t)b * in + k1));
         rq.r0[t] = h2f(ldg(pr.rin + k0));
         rq.r1[t] = h2f(ldg(pr.rin + k1));
-        rq.s0[t] = pr.s_in ? ldg(pr.s_in + k0) : 1.f;
-        rq.s1[t] = pr.s_in ? ldg(pr.s_in + k1) : 1.f;
+        if constexpr (decltype(with_s)::value) {
+          rq.s0[t] = ldg(pr.s_in + k0);
+          rq.s1[t] = ldg(pr.s_in + k1);
+        } else {
+          rq.s0[t] = 1.f;
+          rq.s1[t] = 1.f;
+        }
       }
-    }
+    };
+    if (pr.s_in) load_tasks(std::true_type{});
+    else load_tasks(std::false_type{});
     rotation_compute(B, n, wave, rq, sm);
     __syncthreads();  // (also waits for unit 0)
 #pragma unroll
