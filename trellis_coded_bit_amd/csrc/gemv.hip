@@ -305,7 +305,6 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
   const int wg_units = __builtin_amdgcn_readfirstlane(wg_u1 - wg_start(blockIdx.x, P.U, P.G));
   const int t2 = wg_u1 - (3 * wg_units) / 4, t1 = wg_u1 - (2 * wg_units) / 4, t0 = wg_u1 - wg_units / 4;
   auto prio_at = [&](int c) { return c >= t0 ? 0 : c >= t1 ? 1 : c >= t2 ? 2 : 3; };
-  set_priority(prio_at(ub));
 
   for (int sb = 0; sb < total; sb += P.kA) {
     const int n = __builtin_amdgcn_readfirstlane(min(P.kA, total - sb));
@@ -337,6 +336,7 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
       if (real) advance();
     };
     prime(0);
+    if (sb == 0) set_priority(prio_at(ub));  // (after the first copy is on its way)
     // Rotation loads: straight-line code (tasks past the last are clamped to it and their
     // values ignored), so all of them are in flight together.
     RotLoads rq;
@@ -426,6 +426,12 @@ template <int KS>
 __global__ __launch_bounds__(kThreads, 4) void gemv_partial_kernel(GemvParams P) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   const Lds sm = lds_carve(lds_raw, P.L.B, P.kA);
+  // The arguments needed before the first code copy, read in one round trip (left alone,
+  // the compiler loads them in several dependent rounds around the early branches).
+  asm volatile("" ::"s"(P.U), "s"(P.G), "s"(P.nI), "s"(P.nJ), "s"(P.kA), "s"(P.L.B), "s"(P.L.in_features),
+               "s"(P.L.out_features), "s"(P.L.single.code), "s"(P.L.single.rin), "s"(P.L.single.s_in),
+               "s"(P.L.x), "s"(P.L.shared_side), "s"(P.L.shared_r), "s"(P.L.shared_s), "s"(P.partials), "s"(P.L.table), "s"(P.L.E),
+               "s"(P.L.routed));
   const int g = blockIdx.x;
   const int u0 = wg_start(g, P.U, P.G), u1 = wg_start(g + 1, P.U, P.G);
   if constexpr (KS != 0) {
