@@ -460,11 +460,40 @@ constexpr int kPartialBatch = 32;  // partial loads a thread issues together
 
 __global__ __launch_bounds__(kThreads) void gemv_finish_kernel(GemvParams P) {
   __shared__ float fin[kMaxB][128];
-  __shared__ int slot_of[kPartialBatch];
+  // all arguments in one early round trip
+  asm volatile("" ::"s"(P.U), "s"(P.G), "s"(P.nI), "s"(P.nJ), "s"(P.maxseg), "s"(P.partials), "s"(P.L.B),
+               "s"(P.L.out_features), "s"(P.L.y), "s"(P.L.table), "s"(P.L.E), "s"(P.L.routed),
+               "s"(P.L.single.rout), "s"(P.L.single.s_out), "s"(P.L.shared_side), "s"(P.L.shared_r),
+               "s"(P.L.shared_s));
   const int B = P.L.B, out = P.L.out_features;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = blockIdx.x;
-  // the output-side vectors are requested first (their loads overlap the partials')
+  // Contributors g_lo..g_hi.  Every contributor after the first starts its range inside
+  // block q, so q is its first segment; only g_lo can reach q at a later segment.  The
+  // partial loads therefore need no table and no barrier: they are issued first.
+  const int g_lo = owner(q * P.nI, P.U, P.G), g_hi = owner((q + 1) * P.nI - 1, P.U, P.G);
+  const int seg_lo = q - wg_start(g_lo, P.U, P.G) / P.nI;
+  float v[kMaxB * 128 / kThreads];
+#pragma unroll
+  for (int i = 0; i < kMaxB * 128 / kThreads; ++i) v[i] = 0.f;
+  for (int gb = g_lo; gb <= g_hi; gb += kPartialBatch) {
+#pragma unroll
+    for (int i = 0; i < kMaxB * 128 / kThreads; ++i) {
+      const int idx = tid + i * kThreads;
+      if (idx < B * 128) {
+        float part[kPartialBatch];
+#pragma unroll
+        for (int t = 0; t < kPartialBatch; ++t) {
+          const int gg = gb + t;
+          const size_t sl = (size_t)gg * P.maxseg + (gg == g_lo ? seg_lo : 0);
+          part[t] = gg <= g_hi ? P.partials[sl * kMaxB * 128 + idx] : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < kPartialBatch; ++t) v[i] += part[t];
+      }
+    }
+  }
+  // the output-side vectors (their loads overlap the partials')
   const int p = q / P.nJ, J = q - p * P.nJ;
   const Problem pr = get_problem(P, p);
   const int c0 = J * 128 + lane, c1 = c0 + 64;
@@ -473,33 +502,6 @@ __global__ __launch_bounds__(kThreads) void gemv_finish_kernel(GemvParams P) {
     sa = h2f(ldg(pr.rout + c0)) * (1.0f / 128.0f);
     sb = h2f(ldg(pr.rout + c1)) * (1.0f / 128.0f);
     if (pr.s_out) { sa *= ldg(pr.s_out + c0); sb *= ldg(pr.s_out + c1); }
-  }
-  const int g_lo = owner(q * P.nI, P.U, P.G), g_hi = owner((q + 1) * P.nI - 1, P.U, P.G);
-  float v[kMaxB * 128 / kThreads];
-#pragma unroll
-  for (int i = 0; i < kMaxB * 128 / kThreads; ++i) v[i] = 0.f;
-  for (int gb = g_lo; gb <= g_hi; gb += kPartialBatch) {
-    // partial slot of each contributor of this batch (index arithmetic fits in 32 bits)
-    __syncthreads();
-    if (tid < kPartialBatch) {
-      const int gg = gb + tid;
-      slot_of[tid] = gg <= g_hi ? gg * P.maxseg + (q - (int)(((unsigned)gg * (unsigned)P.U) / (unsigned)P.G) / P.nI) : -1;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kMaxB * 128 / kThreads; ++i) {
-      const int idx = tid + i * kThreads;
-      if (idx < B * 128) {
-        float part[kPartialBatch];
-#pragma unroll
-        for (int t = 0; t < kPartialBatch; ++t) {
-          const int sl = slot_of[t];
-          part[t] = sl >= 0 ? P.partials[(size_t)sl * kMaxB * 128 + idx] : 0.f;
-        }
-#pragma unroll
-        for (int t = 0; t < kPartialBatch; ++t) v[i] += part[t];
-      }
-    }
   }
 #pragma unroll
   for (int i = 0; i < kMaxB * 128 / kThreads; ++i) {
