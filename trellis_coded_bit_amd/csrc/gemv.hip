@@ -177,8 +177,19 @@ __device__ __forceinline__ void rotation_compute(int B, int n, int wave, const R
   }
 }
 
+// Workgroup barrier for LDS traffic only: the waves' code copies in flight are not waited
+// for (a plain __syncthreads would wait for every outstanding vector memory operation).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // End of a segment (the workgroup's share of column block q): reduce the waves'
-// accumulators and store the partial (not waited for: loads in flight keep streaming).
+// accumulators and store the partial (not waited for: code copies in flight keep streaming).
 __device__ __forceinline__ void publish_partial(const GemvParams &P, const Lds &sm, int q, floatx4 (&acc)[8]) {
   const int B = P.L.B;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -192,7 +203,7 @@ __device__ __forceinline__ void publish_partial(const GemvParams &P, const Lds &
   }
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();
+  lds_barrier();
   const int g = blockIdx.x;
   const int seg = q - wg_start(g, P.U, P.G) / P.nI;
   float *part = P.partials + ((size_t)g * P.maxseg + seg) * kMaxB * 128;
@@ -202,7 +213,7 @@ __device__ __forceinline__ void publish_partial(const GemvParams &P, const Lds &
     for (int w = 1; w < kWaves; ++w) v += sm.red[w * B * 128 + idx];
     part[idx] = v;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // ---------------------------------------------------------------------------------------
