@@ -437,6 +437,9 @@ template <int KS>
 __global__ __launch_bounds__(kThreads, 4) void gemv_partial_kernel(GemvParams P) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   const Lds sm = lds_carve(lds_raw, P.L.B, P.kA);
+  // Top issue priority from the start: a workgroup dispatched after its CU's others are
+  // already decoding would otherwise run its prologue at the lowest priority, behind them.
+  __builtin_amdgcn_s_setprio(3);
   // The arguments needed before the first code copy, read in one round trip (left alone,
   // the compiler loads them in several dependent rounds around the early branches).
   asm volatile("" ::"s"(P.U), "s"(P.G), "s"(P.nI), "s"(P.nJ), "s"(P.kA), "s"(P.L.B), "s"(P.L.in_features),
