@@ -125,6 +125,33 @@ def _capture(torch, fn):
     return g
 
 
+class LayerStack:
+    """HIP graphs of consecutive steps, one weight copy per step (copy i % R for step i), as
+    the layers of a model follow one another in one captured decode pass.  run(n) replays
+    exactly n steps: full graphs of R steps, then one graph of the remainder."""
+
+    def __init__(self, torch, step, R):
+        self.torch, self.step, self.R = torch, step, R
+        self.graphs = {}
+
+    def _graph(self, n):
+        if n not in self.graphs:
+            self.graphs[n] = _capture(self.torch, lambda: [self.step(i) for i in range(n)])
+        return self.graphs[n]
+
+    def prepare(self, *counts):
+        for n in counts:
+            if n % self.R:
+                self._graph(n % self.R)
+        self._graph(self.R)
+
+    def run(self, n):
+        for _ in range(n // self.R):
+            self._graph(self.R).replay()
+        if n % self.R:
+            self._graph(n % self.R).replay()
+
+
 def run_dense(args, torch, tb, synth):
     """The dense-MLP decode step: gate and up share their input, so they run as one launch
     over a two-entry layer table (trellis_moe_gemv, per-entry K); down is one trellis_gemv."""
@@ -158,19 +185,19 @@ def run_dense(args, torch, tb, synth):
         gate_up(i)
         down(i)
 
-    # eager warm-up, then one HIP graph per weight copy (a step = one graph replay)
+    # eager warm-up, then HIP graphs of consecutive steps over the weight copies (R steps per
+    # graph: the MLPs of R layers in a row, as in one captured decode pass of a model)
     for i in range(R):
         step(i)
     torch.cuda.synchronize()
-    graphs = [_capture(torch, lambda i=i: step(i)) for i in range(R)]
-    for i in range(args.warmup):
-        graphs[i % R].replay()
+    stack = LayerStack(torch, step, R)
+    stack.prepare(args.warmup, args.steps)
+    stack.run(args.warmup)
     torch.cuda.synchronize()
     t_s = torch.cuda.Event(enable_timing=True)
     t_e = torch.cuda.Event(enable_timing=True)
     t_s.record()
-    for i in range(args.steps):
-        graphs[i % R].replay()
+    stack.run(args.steps)
     t_e.record()
     torch.cuda.synchronize()
     ms_step = t_s.elapsed_time(t_e) / args.steps
@@ -198,7 +225,7 @@ def run_dense(args, torch, tb, synth):
         "dtype": "fp16", "data": "synthetic",
         "config": {"workload": "dense MLP decode, batch 1: gate K2 5120x17408 + up K3 5120x17408 (one "
                                "trellis_moe_gemv launch over a 2-entry table, shared x) + down K3 17408x5120 "
-                               "(trellis_gemv), replayed as a HIP graph",
+                               "(trellis_gemv); steps over 13 weight copies captured as consecutive layers in HIP graphs",
                    "global_batch": 1, "code_bytes_per_step": code_bytes, "weight_copies_rotated": R,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -253,23 +280,22 @@ def run_small_batch(args, torch, tb, synth, B):
         for n in names:
             tb.trellis_gemv(copies[i % R][n], xs[n], out=ys[n], ws=ws)
 
-    # one HIP graph per weight copy, a step = one graph replay (as for the dense step)
+    # HIP graphs of consecutive steps over the weight copies (as for the dense step)
     for i in range(R):
         step(i)
     torch.cuda.synchronize()
-    graphs = [_capture(torch, lambda i=i: step(i)) for i in range(R)]
-    for i in range(args.warmup):
-        graphs[i % R].replay()
+    stack = LayerStack(torch, step, R)
+    stack.prepare(args.warmup, args.steps)
+    stack.run(args.warmup)
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
-    for i in range(args.steps):
-        graphs[i % R].replay()
+    stack.run(args.steps)
     e.record()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / args.steps
     return {"workload": f"small-batch decode K2 B={B} (qkv 5120x10240, z 5120x6144, out 6144x5120; "
-                        "three trellis_gemv per step, HIP graph)", "ms_per_step": round(ms, 5),
+                        "three trellis_gemv per step; consecutive steps over the weight copies in HIP graphs)", "ms_per_step": round(ms, 5),
             "code_GBps": round(code_bytes / (ms * 1e-3) / 1e9, 1),
             "effective_weight_tflops": round(2 * B * sum(wl.layers[n].in_features * wl.layers[n].out_features
                                                        for n in names) / (ms * 1e-3) / 1e12, 3)}
