@@ -216,7 +216,8 @@ typedef floatx4 Acc[4][8];
 
 // Output Hadamard, scales and stores for tile (mt, nt).  Lane holds rows
 // 64*wave + 16*mb + 4*(lane >> 4) + r and columns 16*nb + (lane & 15).
-__device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int mt, int nt) {
+// `stage`: 1 KB of LDS private to the wave (the B ring is idle during the epilogue).
+__device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int mt, int nt, uint16_t *stage) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n16 = lane & 15;
   float sv[8];
 #pragma unroll
@@ -226,7 +227,6 @@ __device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int m
     if (P.s_out) s *= P.s_out[col];
     sv[nb] = s;
   }
-  const int row0 = mt * kMT + 64 * wave + 4 * (lane >> 4);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
@@ -259,12 +259,16 @@ __device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int m
         p = lane_xor<8>(v[nb]);
         v[nb] = (lane & 8) ? (p - v[nb]) : (v[nb] + p);
       }
-      const int row = row0 + 16 * mb + r;
-      if (row < P.M) {
-        uint16_t *yr = P.y + (size_t)row * P.out + nt * kNT + n16;
+      // The wave's four rows of this (mb, r) go through LDS so that every lane stores 16
+      // contiguous bytes (8 columns): lane l takes row l >> 4, columns 8 * (l & 15) ...
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) yr[16 * nb] = f2h(v[nb] * sv[nb]);
-      }
+      for (int nb = 0; nb < 8; ++nb) stage[(lane >> 4) * 128 + 16 * nb + n16] = f2h(v[nb] * sv[nb]);
+      __builtin_amdgcn_wave_barrier();
+      const u32x4 out8 = *reinterpret_cast<const u32x4 *>(stage + (lane >> 4) * 128 + 8 * n16);
+      __builtin_amdgcn_wave_barrier();  // the next group's writes come after these reads
+      const int row = mt * kMT + 64 * wave + 16 * mb + 4 * (lane >> 4) + r;
+      if (row < P.M)
+        *reinterpret_cast<u32x4 *>(P.y + (size_t)row * P.out + nt * kNT + 8 * n16) = out8;
     }
   }
 }
@@ -457,6 +461,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
   __shared__ __attribute__((aligned(16))) u32x4 ring[2][8][64];         // decoded B operands
   __shared__ __attribute__((aligned(16))) u32x4 cring[kWaves][4 * 2 * 32 / 4];  // staged codes
   __shared__ uint32_t arrivals;
+  // epilogue staging: the wave's own 1 KB of B ring slot 0 (idle between pieces)
+  uint16_t *stage = reinterpret_cast<uint16_t *>(&ring[0][threadIdx.x >> 6][0]);
   const int g = xcd_range(blockIdx.x, P.G);
   long long it = range_start(P, g);
   const long long end = range_start(P, g + 1);
@@ -470,7 +476,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
     run_piece<K>(P, ring, cring, t, k0, k1, acc, signal);
     signal = -1;
     if (k0 == 0 && k1 == P.S) {
-      finish_tile(P, acc, t / P.nNT, t % P.nNT);
+      finish_tile(P, acc, t / P.nNT, t % P.nNT, stage);
     } else {
       const long long ts = (long long)t * P.S;
       const int g0 = range_owner(P, ts), g1 = range_owner(P, ts + P.S - 1);
@@ -497,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
           __syncthreads();
           const int c = g0 + g1 - g;  // the other contributor
           add_partial(P, 2 * c + (range_start(P, c) >= ts ? 0 : 1), acc, false);
-          finish_tile(P, acc, t / P.nNT, t % P.nNT);
+          finish_tile(P, acc, t / P.nNT, t % P.nNT, stage);
         }
       } else {
         // Three or more contributors (ranges shorter than a tile): every one stores its
@@ -513,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
           // starts inside t, else its last piece (slot 2c + 1).
           for (int c = g0; c <= g1; ++c)
             add_partial(P, 2 * c + (range_start(P, c) >= ts ? 0 : 1), acc, c == g0);
-          finish_tile(P, acc, t / P.nNT, t % P.nNT);
+          finish_tile(P, acc, t / P.nNT, t % P.nNT, stage);
         }
       }
     }
