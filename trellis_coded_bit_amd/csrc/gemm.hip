@@ -464,23 +464,29 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
   // epilogue staging: the wave's own 1 KB of B ring slot 0 (idle between pieces)
   uint16_t *stage = reinterpret_cast<uint16_t *>(&ring[0][threadIdx.x >> 6][0]);
   const int g = xcd_range(blockIdx.x, P.G);
-  long long it = range_start(P, g);
+  const long long it0 = range_start(P, g);
   const long long end = range_start(P, g + 1);
-  bool first = true;
   int signal = -1;  // split tile whose stored partial is still to be published
-  while (it < end) {
-    const int t = (int)(it / P.S);
-    const int k0 = (int)(it - (long long)t * P.S);
-    const int k1 = (int)min((long long)P.S, (long long)k0 + (end - it));
+  // The range covers tiles tf..tl.  A split tile's two contributors meet in the middle of
+  // the tile: one at the end of its range, the other at the start of its range.  The piece
+  // at the end of the range is done FIRST (then the start piece, then the whole tiles), so
+  // both contributors of a split tile reach it early and its partial tile is stored and
+  // added while other workgroups still compute, rather than in the kernel's tail.
+  const int tf = it0 < end ? (int)(it0 / P.S) : 0, tl = it0 < end ? (int)((end - 1) / P.S) : -1;
+  const bool end_first = tl > tf && end - (long long)tl * P.S < P.S;
+  for (int j = 0; j <= tl - tf; ++j) {
+    const int t = end_first ? (j == 0 ? tl : tf + j - 1) : tf + j;
+    const long long ts = (long long)t * P.S;
+    const int k0 = t == tf ? (int)(it0 - ts) : 0;
+    const int k1 = t == tl ? (int)(end - ts) : P.S;
     Acc acc;
     run_piece<K>(P, ring, cring, t, k0, k1, acc, signal);
     signal = -1;
     if (k0 == 0 && k1 == P.S) {
       finish_tile(P, acc, t / P.nNT, t % P.nNT, stage);
     } else {
-      const long long ts = (long long)t * P.S;
       const int g0 = range_owner(P, ts), g1 = range_owner(P, ts + P.S - 1);
-      const int own = 2 * g + (first ? 0 : 1);
+      const int own = 2 * g + (t == tf ? 0 : 1);  // slot 2g: the range's start piece
       if (g1 == g0 + 1) {
         // Two contributors.  Counters (arrived, stored) per tile.  The first to arrive
         // stores its partial tile and publishes it later (start of its next piece, or
@@ -515,16 +521,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
           arrivals = __hip_atomic_fetch_add(P.counters + 2 * t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         if (arrivals == (uint32_t)(g1 - g0)) {
-          // A contributor's piece of tile t is its first piece (slot 2c) when its range
-          // starts inside t, else its last piece (slot 2c + 1).
+          // A contributor's piece of tile t is the start piece of its range (slot 2c) when
+          // its range starts inside t, else the end piece (slot 2c + 1).
           for (int c = g0; c <= g1; ++c)
             add_partial(P, 2 * c + (range_start(P, c) >= ts ? 0 : 1), acc, c == g0);
           finish_tile(P, acc, t / P.nNT, t % P.nNT, stage);
         }
       }
     }
-    it += k1 - k0;
-    first = false;
   }
   if (signal >= 0) {
     __syncthreads();  // the stores of the last piece's partial have completed
