@@ -64,17 +64,18 @@ struct GemmParams {
   int S;               // k-step pairs per tile (the unit of the ranges)
   int nNT;             // column tiles
   int G;               // workgroups
-  long long q;         // iterations per workgroup (the first r take one more)
+  int q;               // iterations per workgroup (the first r take one more)
   int r;
 };
 
-__device__ __forceinline__ long long range_start(const GemmParams &P, int g) {
-  return (long long)g * P.q + (g < P.r ? g : P.r);
+// Iteration counts fit in 32 bits (checked at launch).
+__device__ __forceinline__ int range_start(const GemmParams &P, int g) {
+  return g * P.q + (g < P.r ? g : P.r);
 }
 
-__device__ __forceinline__ int range_owner(const GemmParams &P, long long i) {
-  const long long big = (long long)P.r * (P.q + 1);
-  return i < big ? (int)(i / (P.q + 1)) : (int)(P.r + (i - big) / P.q);
+__device__ __forceinline__ int range_owner(const GemmParams &P, int i) {
+  const int big = P.r * (P.q + 1);
+  return i < big ? i / (P.q + 1) : P.r + (i - big) / P.q;
 }
 
 // Workgroup b runs on XCD b % 8; give each XCD a contiguous block of ranges.
@@ -216,9 +217,12 @@ typedef floatx4 Acc[4][8];
 
 // Output Hadamard, scales and stores for tile (mt, nt).  Lane holds rows
 // 64*wave + 16*mb + 4*(lane >> 4) + r and columns 16*nb + (lane & 15).
-// `stage`: 1 KB of LDS private to the wave (the B ring is idle during the epilogue).
-__device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int mt, int nt, uint16_t *stage) {
+// Staging through LDS uses the wave's own 1 KB of B ring slot 0 (idle between pieces).
+__device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int mt, int nt, u32x4 (*ring)[8][64]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n16 = lane & 15;
+  const float sg1 = (lane & 1) ? -1.f : 1.f, sg2 = (lane & 2) ? -1.f : 1.f;
+  const float sg4 = (lane & 4) ? -1.f : 1.f, sg8 = (lane & 8) ? -1.f : 1.f;
+  uint16_t *stage = reinterpret_cast<uint16_t *>(&ring[0][__builtin_amdgcn_readfirstlane(wave)][0]);
   float sv[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
@@ -246,18 +250,14 @@ __device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int m
           }
         }
       }
-      // column strides 1, 2, 4, 8: lanes inside each group of 16
+      // column strides 1, 2, 4, 8: lanes inside each group of 16 (partner + own where the
+      // stride bit is clear, partner - own where it is set).
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
-        float p;
-        p = lane_xor<1>(v[nb]);
-        v[nb] = (lane & 1) ? (p - v[nb]) : (v[nb] + p);
-        p = lane_xor<2>(v[nb]);
-        v[nb] = (lane & 2) ? (p - v[nb]) : (v[nb] + p);
-        p = lane_xor<4>(v[nb]);
-        v[nb] = (lane & 4) ? (p - v[nb]) : (v[nb] + p);
-        p = lane_xor<8>(v[nb]);
-        v[nb] = (lane & 8) ? (p - v[nb]) : (v[nb] + p);
+        v[nb] = lane_xor<1>(v[nb]) + sg1 * v[nb];
+        v[nb] = lane_xor<2>(v[nb]) + sg2 * v[nb];
+        v[nb] = lane_xor<4>(v[nb]) + sg4 * v[nb];
+        v[nb] = lane_xor<8>(v[nb]) + sg8 * v[nb];
       }
       // The wave's four rows of this (mb, r) go through LDS so that every lane stores 16
       // contiguous bytes (8 columns): lane l takes row l >> 4, columns 8 * (l & 15) ...
@@ -461,29 +461,27 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
   __shared__ __attribute__((aligned(16))) u32x4 ring[2][8][64];         // decoded B operands
   __shared__ __attribute__((aligned(16))) u32x4 cring[kWaves][4 * 2 * 32 / 4];  // staged codes
   __shared__ uint32_t arrivals;
-  // epilogue staging: the wave's own 1 KB of B ring slot 0 (idle between pieces)
-  uint16_t *stage = reinterpret_cast<uint16_t *>(&ring[0][threadIdx.x >> 6][0]);
   const int g = xcd_range(blockIdx.x, P.G);
-  const long long it0 = range_start(P, g);
-  const long long end = range_start(P, g + 1);
+  const int it0 = range_start(P, g);
+  const int end = range_start(P, g + 1);
   int signal = -1;  // split tile whose stored partial is still to be published
   // The range covers tiles tf..tl.  A split tile's two contributors meet in the middle of
   // the tile: one at the end of its range, the other at the start of its range.  The piece
   // at the end of the range is done FIRST (then the start piece, then the whole tiles), so
   // both contributors of a split tile reach it early and its partial tile is stored and
   // added while other workgroups still compute, rather than in the kernel's tail.
-  const int tf = it0 < end ? (int)(it0 / P.S) : 0, tl = it0 < end ? (int)((end - 1) / P.S) : -1;
-  const bool end_first = tl > tf && end - (long long)tl * P.S < P.S;
+  const int tf = it0 < end ? it0 / P.S : 0, tl = it0 < end ? (end - 1) / P.S : -1;
+  const bool end_first = tl > tf && end - tl * P.S < P.S;
   for (int j = 0; j <= tl - tf; ++j) {
     const int t = end_first ? (j == 0 ? tl : tf + j - 1) : tf + j;
-    const long long ts = (long long)t * P.S;
-    const int k0 = t == tf ? (int)(it0 - ts) : 0;
-    const int k1 = t == tl ? (int)(end - ts) : P.S;
+    const int ts = t * P.S;
+    const int k0 = t == tf ? it0 - ts : 0;
+    const int k1 = t == tl ? end - ts : P.S;
     Acc acc;
     run_piece<K>(P, ring, cring, t, k0, k1, acc, signal);
     signal = -1;
     if (k0 == 0 && k1 == P.S) {
-      finish_tile(P, acc, t / P.nNT, t % P.nNT, stage);
+      finish_tile(P, acc, t / P.nNT, t % P.nNT, ring);
     } else {
       const int g0 = range_owner(P, ts), g1 = range_owner(P, ts + P.S - 1);
       const int own = 2 * g + (t == tf ? 0 : 1);  // slot 2g: the range's start piece
@@ -509,7 +507,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
           __syncthreads();
           const int c = g0 + g1 - g;  // the other contributor
           add_partial(P, 2 * c + (range_start(P, c) >= ts ? 0 : 1), acc, false);
-          finish_tile(P, acc, t / P.nNT, t % P.nNT, stage);
+          finish_tile(P, acc, t / P.nNT, t % P.nNT, ring);
         }
       } else {
         // Three or more contributors (ranges shorter than a tile): every one stores its
@@ -525,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
           // its range starts inside t, else the end piece (slot 2c + 1).
           for (int c = g0; c <= g1; ++c)
             add_partial(P, 2 * c + (range_start(P, c) >= ts ? 0 : 1), acc, c == g0);
-          finish_tile(P, acc, t / P.nNT, t % P.nNT, stage);
+          finish_tile(P, acc, t / P.nNT, t % P.nNT, ring);
         }
       }
     }
@@ -551,8 +549,8 @@ int device_cu_count() {
 
 struct Plan {
   int S, nNT, T, G;
-  long long I, q;
-  int r;
+  long long I;
+  int q, r;
   size_t xh_bytes, partials_off, counters_off, bytes;
 };
 
@@ -573,7 +571,7 @@ Plan plan(int in_features, int out_features, int M) {
   if (G > p.I) G = p.I;
   if (G < 1) G = 1;
   p.G = (int)G;
-  p.q = p.I / G;
+  p.q = (int)(p.I / G);
   p.r = (int)(p.I % G);
   p.xh_bytes = (size_t)((M + 15) / 16) * 16 * in_features * 2;  // whole 16-row blocks
   p.partials_off = p.xh_bytes;
@@ -595,6 +593,7 @@ hipError_t launch_gemm(const trellis_linear &L, const uint16_t *x, int M, uint16
   const Plan p = plan(L.in_features, L.out_features, M);
   if (ws_bytes < p.bytes) return hipErrorInvalidValue;
   if (p.G > (1 << 20)) return hipErrorInvalidValue;
+  if (p.I >= (1LL << 31)) return hipErrorInvalidValue;  // 32-bit iteration arithmetic
   uint16_t *xh = static_cast<uint16_t *>(ws);
   uint32_t *counters = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + p.counters_off);
   if ((long long)(M + 15) / 16 * (L.in_features / 128) >= (1LL << 31)) return hipErrorInvalidValue;

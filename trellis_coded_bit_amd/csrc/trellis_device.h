@@ -94,27 +94,31 @@ __device__ __forceinline__ uint16_t f2h(float f) {
 }
 
 // Value of lane (lane ^ m) for m = 1, 2, 4, 8 (DPP within rows of 16), 16 (swizzle within
-// halves of the wave) and 32 (bpermute).
+// halves of the wave) and 32 (bpermute).  The DPP forms (every source lane valid) are
+// written as updates with bound_ctrl so the compiler can fold the move into the VALU
+// operation that consumes it.
 template <int M>
 __device__ __forceinline__ float lane_xor(float v) {
   const int x = __builtin_bit_cast(int, v);
   int r;
-  if constexpr (M == 1) r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
-  else if constexpr (M == 2) r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  if constexpr (M == 1) r = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true);   // quad_perm 1,0,3,2
+  else if constexpr (M == 2) r = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
   else if constexpr (M == 4)  // row_half_mirror (i -> 7 - i) then quad_perm 3,2,1,0: i -> i ^ 4
-    r = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false), 0x1B, 0xF, 0xF, false);
-  else if constexpr (M == 8) r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror 8
-  else if constexpr (M == 16) r = __builtin_amdgcn_ds_swizzle(x, 0x401F);             // xor 16
+    r = __builtin_amdgcn_update_dpp(0, __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, true), 0x1B, 0xF, 0xF,
+                                    true);
+  else if constexpr (M == 8) r = __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, true);  // row_ror 8
+  else if constexpr (M == 16) r = __builtin_amdgcn_ds_swizzle(x, 0x401F);                 // xor 16
   else r = __shfl_xor(x, M, 64);
   return __builtin_bit_cast(float, r);
 }
 
+// One butterfly stage across lanes: partner + own on the lane whose stride bit is clear,
+// partner - own on the other (one sign select and one add that takes the partner by DPP).
 template <int M>
 __device__ __forceinline__ void fwht_stage(float &a, float &b, int lane) {
-  const float pa = lane_xor<M>(a), pb = lane_xor<M>(b);
-  const bool up = (lane & M) != 0;
-  a = up ? (pa - a) : (a + pa);
-  b = up ? (pb - b) : (b + pb);
+  const float sg = (lane & M) ? -1.f : 1.f;
+  a = lane_xor<M>(a) + sg * a;
+  b = lane_xor<M>(b) + sg * b;
 }
 
 // Unnormalised Sylvester Hadamard butterfly over 128 values held two per lane: element
