@@ -217,12 +217,24 @@ typedef floatx4 Acc[4][8];
 
 // Output Hadamard, scales and stores for tile (mt, nt).  Lane holds rows
 // 64*wave + 16*mb + 4*(lane >> 4) + r and columns 16*nb + (lane & 15).
+// Raw buffer resource over `bytes` bytes at `base` (loads past the end return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, long long bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
 // Staging through LDS uses the wave's own 1 KB of B ring slot 0 (idle between pieces).
 __device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int mt, int nt, u32x4 (*ring)[8][64]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n16 = lane & 15;
+  const int lane = threadIdx.x & 63, n16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const float sg1 = (lane & 1) ? -1.f : 1.f, sg2 = (lane & 2) ? -1.f : 1.f;
   const float sg4 = (lane & 4) ? -1.f : 1.f, sg8 = (lane & 8) ? -1.f : 1.f;
-  uint16_t *stage = reinterpret_cast<uint16_t *>(&ring[0][__builtin_amdgcn_readfirstlane(wave)][0]);
+  uint16_t *stage = reinterpret_cast<uint16_t *>(&ring[0][wave][0]);
+  // the wave's 64 rows of the tile's output (uniform); stores to rows past M fall outside
+  // the buffer range and are dropped
+  const int wrow0 = mt * kMT + 64 * wave;
+  const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(P.y + (size_t)wrow0 * P.out + nt * kNT,
+                                                (long long)(P.M - wrow0) * P.out * 2 - nt * kNT * 2);
   float sv[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
@@ -261,23 +273,20 @@ __device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int m
       }
       // The wave's four rows of this (mb, r) go through LDS so that every lane stores 16
       // contiguous bytes (8 columns): lane l takes row l >> 4, columns 8 * (l & 15) ...
+      // (The lane index is re-derived here: kept live across the groups it gets spilled.)
+      int l = threadIdx.x & 63;
+      asm volatile("" : "+v"(l));
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) stage[(lane >> 4) * 128 + 16 * nb + n16] = f2h(v[nb] * sv[nb]);
+      for (int nb = 0; nb < 8; ++nb) stage[(l >> 4) * 128 + 16 * nb + (l & 15)] = f2h(v[nb] * sv[nb]);
       __builtin_amdgcn_wave_barrier();
-      const u32x4 out8 = *reinterpret_cast<const u32x4 *>(stage + (lane >> 4) * 128 + 8 * n16);
+      const u32x4 out8 = *reinterpret_cast<const u32x4 *>(stage + (l >> 4) * 128 + 8 * (l & 15));
       __builtin_amdgcn_wave_barrier();  // the next group's writes come after these reads
-      const int row = mt * kMT + 64 * wave + 16 * mb + 4 * (lane >> 4) + r;
-      if (row < P.M)
-        *reinterpret_cast<u32x4 *>(P.y + (size_t)row * P.out + nt * kNT + 8 * n16) = out8;
+      const int rr = 16 * mb + 4 * (l >> 4) + r;  // row inside the wave's 64
+      __builtin_amdgcn_raw_buffer_store_b128(out8, ry, (uint32_t)(rr * P.out * 2 + 16 * (l & 15)), 0, 0);
     }
   }
 }
 
-// Raw buffer resource over `bytes` bytes at `base` (loads past the end return zero).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, long long bytes) {
-  const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
-}
 
 // Partial tiles in the workspace: slot-major, then wave, (mb, nb), lane, four floats each
 // (coalesced 1 KB per instruction).  They are written and read with device-scope
@@ -480,9 +489,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
     Acc acc;
     run_piece<K>(P, ring, cring, t, k0, k1, acc, signal);
     signal = -1;
-    if (k0 == 0 && k1 == P.S) {
-      finish_tile(P, acc, t / P.nNT, t % P.nNT, ring);
-    } else {
+    bool finish = k0 == 0 && k1 == P.S;  // one epilogue call site (register allocation)
+    if (!finish) {
       const int g0 = range_owner(P, ts), g1 = range_owner(P, ts + P.S - 1);
       const int own = 2 * g + (t == tf ? 0 : 1);  // slot 2g: the range's start piece
       if (g1 == g0 + 1) {
@@ -507,7 +515,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
           __syncthreads();
           const int c = g0 + g1 - g;  // the other contributor
           add_partial(P, 2 * c + (range_start(P, c) >= ts ? 0 : 1), acc, false);
-          finish_tile(P, acc, t / P.nNT, t % P.nNT, ring);
+          finish = true;
         }
       } else {
         // Three or more contributors (ranges shorter than a tile): every one stores its
@@ -523,10 +531,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
           // its range starts inside t, else the end piece (slot 2c + 1).
           for (int c = g0; c <= g1; ++c)
             add_partial(P, 2 * c + (range_start(P, c) >= ts ? 0 : 1), acc, c == g0);
-          finish_tile(P, acc, t / P.nNT, t % P.nNT, ring);
+          finish = true;
         }
       }
     }
+    if (finish) finish_tile(P, acc, t / P.nNT, t % P.nNT, ring);
   }
   if (signal >= 0) {
     __syncthreads();  // the stores of the last piece's partial have completed
