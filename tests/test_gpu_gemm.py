@@ -82,3 +82,18 @@ def test_gemm_matches_gemv_rows():
     yg = tb.trellis_gemm(L, to_dev(x)).cpu().numpy()
     yv = tb.trellis_gemv(L, to_dev(x)).cpu().numpy()
     assert rel_l2(yg, yv) < 1e-3
+
+
+@pytest.mark.parametrize("M,n_in,n_out", [(17, 256, 384), (300, 128, 256), (513, 128, 128)])
+def test_gemm_writes_only_m_rows(M, n_in, n_out):
+    """The output rows past M (the tile's padding) are never written: y sits at the start of
+    a larger buffer whose guard rows must keep their values."""
+    log_case(f"gemm guard rows M={M} {n_in}x{n_out}")
+    lin = synth.make_linear(np.random.SeedSequence([7, M, n_in, n_out]), 3, n_in, n_out)
+    x = synth.make_x(np.random.SeedSequence([M, 9]), M, n_in)
+    big = torch.full((M + 64, n_out), 12345.0, dtype=torch.float16, device="cuda")
+    y = tb.trellis_gemm(dev_linear(lin), to_dev(x), out=big[:M])
+    torch.cuda.synchronize()
+    assert y.data_ptr() == big.data_ptr()
+    assert bool((big[M:] == 12345.0).all())
+    assert rel_l2(big[:M].cpu().numpy(), O.forward_linear(lin, x)) < REL_L2_TOL

@@ -264,13 +264,15 @@ __device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int m
       }
       // column strides 1, 2, 4, 8: lanes inside each group of 16 (partner + own where the
       // stride bit is clear, partner - own where it is set).
+      // (stage by stage over the eight values: eight independent DPP chains in flight)
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        v[nb] = lane_xor<1>(v[nb]) + sg1 * v[nb];
-        v[nb] = lane_xor<2>(v[nb]) + sg2 * v[nb];
-        v[nb] = lane_xor<4>(v[nb]) + sg4 * v[nb];
-        v[nb] = lane_xor<8>(v[nb]) + sg8 * v[nb];
-      }
+      for (int nb = 0; nb < 8; ++nb) v[nb] = lane_xor<1>(v[nb]) + sg1 * v[nb];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) v[nb] = lane_xor<2>(v[nb]) + sg2 * v[nb];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) v[nb] = lane_xor<4>(v[nb]) + sg4 * v[nb];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) v[nb] = lane_xor<8>(v[nb]) + sg8 * v[nb];
       // The wave's four rows of this (mb, r) go through LDS so that every lane stores 16
       // contiguous bytes (8 columns): lane l takes row l >> 4, columns 8 * (l & 15) ...
       // (The lane index is re-derived here: kept live across the groups it gets spilled.)
