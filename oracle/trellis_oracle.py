@@ -10,9 +10,10 @@ Sources (cited by page title and section; no line numbers):
   the tile / tensor-core permutation paragraph and the Shannon-bound paragraph.
 * [EXLR8]  the EXLR8 format page -- the rotation paragraphs (Q = signs x Hadamard), the
   tile-coding paragraph (Viterbi over a 16-bit-state trellis), the shared hidden-side
-  rotation paragraph.
+  rotation paragraph, the calibration paragraph (the expert MLP's activation) and the
+  width-manifest paragraph (per-half widths).
 
-Readings taken where the pages are silent or disagree are named A1..A20 in the
+Readings taken where the pages are silent or disagree are named A1..A21 in the
 docstrings and listed in the design notes.  Every function here follows the plain
 definition; nothing is blocked, fused or reordered beyond what the definition states.
 """
@@ -296,6 +297,49 @@ def moe_forward(layer, routed: Iterable[int], x_token: np.ndarray, x_down: np.nd
         d.append(forward(de.code, de.K, de.rin, layer.r_hidden_out, de.s_in, layer.s_hidden_out,
                          x_down[k:k + 1], cb_d)[0])
     return np.stack(g), np.stack(u), np.stack(d)
+
+
+def silu(z) -> np.ndarray:
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z)), float64.
+
+    [EXLR8] calibration paragraph: the down projection's input is silu(gate x) times up x,
+    elementwise.  For z below about -709 exp(-z) overflows to inf and the quotient is -0,
+    the correctly rounded limit.
+    """
+    z = np.asarray(z, np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def moe_mlp_forward(layer, routed: Sequence[int], router_w: Sequence[float], x_token: np.ndarray,
+                    return_act: bool = False):
+    """Routed-expert MLP of one token, float64:  y = sum_k w_k * down_e(a_k),  e = routed[k],
+    a_k = silu(gate_e(x)) * up_e(x)  (elementwise, [inter]).
+
+    [EXLR8] calibration paragraph (a = silu(gate x) . up x, gate and up share the 6144-wide
+    input x); width-manifest paragraph (gate/up stored per half: a half is 128 consecutive
+    intermediate channels with its own width; down one width per expert); shared-rotation
+    paragraph (the hidden side's vectors are one per layer).  Each linear is forward() above
+    with that side's vectors: gate/up halves take the shared hidden input vectors and their
+    own output vectors, down takes its own input vectors and the shared hidden output ones.
+    gate_e(x) is the concatenation of its halves' outputs in half order.  Reading A21: the
+    router weights are inputs (the pages fix no router), combined as a weighted sum of the
+    experts' outputs.  Returns y [hidden] (and the activations a [n, inter] if asked).
+    """
+    x = np.atleast_2d(np.asarray(x_token))
+    acts, y = [], np.zeros(layer.hidden)
+    for k, e in enumerate(routed):
+        g = np.concatenate([forward(l.code, l.K, layer.r_hidden_in, l.rout, layer.s_hidden_in, l.s_out, x)[0]
+                            for l in layer.gate[e]])
+        u = np.concatenate([forward(l.code, l.K, layer.r_hidden_in, l.rout, layer.s_hidden_in, l.s_out, x)[0]
+                            for l in layer.up[e]])
+        a = silu(g) * u
+        d = layer.down[e]
+        y = y + float(router_w[k]) * forward(d.code, d.K, d.rin, layer.r_hidden_out, d.s_in,
+                                             layer.s_hidden_out, a[None, :])[0]
+        acts.append(a)
+    act = np.stack(acts) if acts else np.zeros((0, layer.inter))
+    return (y, act) if return_act else y
 
 
 # ----------------------------------------------------------------------------------------

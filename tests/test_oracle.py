@@ -323,6 +323,106 @@ def test_shannon_band_catches_offset_decode():
 
 
 # ---------------------------------------------------------------------------------------
+# Routed-expert MLP ([EXLR8] calibration and width-manifest paragraphs)
+# ---------------------------------------------------------------------------------------
+
+def _small_mlp(seed=0, halves=2):
+    return synth.moe_mlp_layer(seed, n_experts=4, hidden=256, inter=256, halves=halves)
+
+
+def test_silu_closed_forms_and_library():
+    """silu(z) = z * sigmoid(z): exact points, the odd-part identity silu(z) - silu(-z) = z,
+    the overflow limits, and scipy's logistic function."""
+    import scipy.special
+    assert O.silu(0.0) == 0.0
+    assert O.silu(math.log(3.0)) == pytest.approx(0.75 * math.log(3.0), rel=1e-15)  # sigmoid(ln 3) = 3/4
+    z = np.linspace(-30, 30, 601)
+    np.testing.assert_allclose(O.silu(z) - O.silu(-z), z, atol=1e-13)
+    np.testing.assert_allclose(O.silu(z), z * scipy.special.expit(z), rtol=1e-14, atol=1e-300)
+    big = O.silu(np.array([-800.0, 800.0]))
+    assert big[0] == 0.0 and big[1] == 800.0 and np.all(np.isfinite(big))
+
+
+def _dense(lin, rin, s_in, rout, s_out):
+    """Dense W [in, out] from the decoded tiles, built with scipy's Hadamard."""
+    H = scipy.linalg.hadamard(128) / math.sqrt(128)
+    w_hat = O.decode_tiles(lin.code, lin.K).astype(np.float64)
+    hl = np.kron(np.eye(w_hat.shape[0] // 128), H)
+    hr = np.kron(np.eye(w_hat.shape[1] // 128), H)
+    su = rin.astype(np.float64) * s_in
+    sv = rout.astype(np.float64) * s_out
+    return su[:, None] * (hl @ w_hat @ hr) * sv[None, :]
+
+
+def test_moe_mlp_equals_dense_composition():
+    """The routed MLP equals sum_k w_k (silu(x Wg) * (x Wu)) Wd with dense matrices built
+    independently: gate/up from their halves side by side with the shared hidden input
+    vectors, down with the shared hidden output vectors."""
+    import scipy.special
+    L = _small_mlp(0)
+    routed, w = [2, 0, 3], [0.5, 0.3, 0.2]
+    x = synth.make_x(np.random.SeedSequence(11), 1, 256)
+    y, act = O.moe_mlp_forward(L, routed, w, x, return_act=True)
+    xf = x.astype(np.float64)
+    ref = np.zeros((1, 256))
+    for k, e in enumerate(routed):
+        Wg = np.hstack([_dense(l, L.r_hidden_in, L.s_hidden_in, l.rout, l.s_out) for l in L.gate[e]])
+        Wu = np.hstack([_dense(l, L.r_hidden_in, L.s_hidden_in, l.rout, l.s_out) for l in L.up[e]])
+        d = L.down[e]
+        Wd = _dense(d, d.rin, d.s_in, L.r_hidden_out, L.s_hidden_out)
+        g, u = xf @ Wg, xf @ Wu
+        a = g * scipy.special.expit(g) * u
+        assert O.rel_l2(act[k], a[0]) < 1e-12
+        ref += w[k] * (a @ Wd)
+    assert O.rel_l2(y, ref[0]) < 1e-12
+
+
+def test_moe_mlp_halves_are_consecutive_channel_slices():
+    """Gate/up stored as two 128-channel halves (same width) give the same MLP as one
+    full-width matrix whose column tiles and output vectors are those halves side by side."""
+    import dataclasses
+    L2 = _small_mlp(1, halves=2)
+    gate, up = [], []
+    for e in range(4):
+        full = []
+        for halves in (L2.gate[e], L2.up[e]):
+            K = 3
+            parts = [dataclasses.replace(h, K=K, code=synth.make_linear(np.random.SeedSequence([e, i, 7]), K, 256, 128).code)
+                     for i, h in enumerate(halves)]
+            full.append(parts)
+        gate.append(full[0])
+        up.append(full[1])
+    Lh = dataclasses.replace(L2, gate=gate, up=up)
+
+    def merged(halves):
+        a, b = halves
+        return dataclasses.replace(a, out_features=256, code=np.concatenate([a.code, b.code], axis=1),
+                                   rout=np.concatenate([a.rout, b.rout]), s_out=np.concatenate([a.s_out, b.s_out]))
+    L1 = dataclasses.replace(Lh, halves=1, gate=[[merged(g)] for g in gate], up=[[merged(u)] for u in up])
+    x = synth.make_x(np.random.SeedSequence(12), 1, 256)
+    y2, a2 = O.moe_mlp_forward(Lh, [1, 3], [0.6, 0.4], x, return_act=True)
+    y1, a1 = O.moe_mlp_forward(L1, [1, 3], [0.6, 0.4], x, return_act=True)
+    np.testing.assert_allclose(a2, a1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(y2, y1, rtol=1e-12, atol=1e-12)
+    # swapping the two halves of every expert changes the result
+    Ls = dataclasses.replace(Lh, gate=[g[::-1] for g in gate], up=[u[::-1] for u in up])
+    assert O.rel_l2(O.moe_mlp_forward(Ls, [1, 3], [0.6, 0.4], x), y1) > 0.1
+
+
+def test_moe_mlp_linear_in_router_weights_and_order_free():
+    L = _small_mlp(2)
+    x = synth.make_x(np.random.SeedSequence(13), 1, 256)
+    routed, w = [3, 1, 2], np.array([0.2, 0.7, 0.1])
+    y = O.moe_mlp_forward(L, routed, w, x)
+    parts = [O.moe_mlp_forward(L, [e], [1.0], x) for e in routed]
+    np.testing.assert_allclose(y, sum(wk * p for wk, p in zip(w, parts)), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O.moe_mlp_forward(L, routed[::-1], w[::-1], x), y, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O.moe_mlp_forward(L, routed, 2 * w, x), 2 * y, rtol=1e-12, atol=1e-12)
+    y0, a0 = O.moe_mlp_forward(L, [], [], x, return_act=True)
+    assert np.all(y0 == 0) and a0.shape == (0, 256)
+
+
+# ---------------------------------------------------------------------------------------
 # Inputs
 # ---------------------------------------------------------------------------------------
 

@@ -190,3 +190,94 @@ def moe_token_inputs(seed: int, hidden: int = HIDDEN_MOE, inner: int = INTER_MOE
     """Token activation x [1, hidden] for gate/up and per-expert down inputs [n_routed, inner]."""
     cx, cd = np.random.SeedSequence([seed, 0x544F4B]).spawn(2)
     return make_x(cx, 1, hidden), make_x(cd, n_routed, inner)
+
+
+# --------------------------------------------------------------------------------------
+# Routed-expert MLP with per-half widths (EXLR8 page: a "half" is 128 of an expert's
+# intermediate channels and the storage unit of gate/up; down has one width per expert).
+# --------------------------------------------------------------------------------------
+
+HALF = 128
+
+
+@dataclasses.dataclass
+class MoEMLPLayer:
+    """E experts; gate/up stored as ``halves`` column slices [hidden -> inter/halves] each
+    with its own width, down [inter -> hidden] with one width per expert.
+
+    The hidden-side vectors are shared by every expert (one per layer); the per-half
+    ``Linear`` objects carry references to the shared input-side arrays (no copies) and
+    their own output-side vectors for their channels.  Down's output-side fields are the
+    shared ``r_hidden_out``/``s_hidden_out`` references.
+    """
+
+    hidden: int
+    inter: int
+    halves: int
+    K_gu: np.ndarray  # int32 [E, halves]: width of half h of expert e (gate and up alike)
+    K_d: np.ndarray  # int32 [E]
+    gate: List[Optional[List[Linear]]]  # [E][halves]
+    up: List[Optional[List[Linear]]]
+    down: List[Optional[Linear]]
+    r_hidden_in: np.ndarray
+    s_hidden_in: np.ndarray
+    r_hidden_out: np.ndarray
+    s_hidden_out: np.ndarray
+
+    def expert_code_bytes(self, e: int) -> int:
+        return (sum(l.code_bytes for l in self.gate[e]) + sum(l.code_bytes for l in self.up[e])
+                + self.down[e].code_bytes)
+
+
+def _half_linear(ss: np.random.SeedSequence, K: int, hidden: int, width: int, r_in, s_in) -> Linear:
+    """One gate/up half: children spawned in the order code, rout, s_out."""
+    c_code, c_rout, c_sout = ss.spawn(3)
+    code = _rng(c_code).integers(0, 1 << 16, size=(hidden // 16, width // 16, 16 * K),
+                                 dtype=np.uint16).view(np.int16)
+    rout = _rng(c_rout).uniform(0.5, 1.5, size=width).astype(np.float16)
+    s_out = _rng(c_sout).normal(1.0, 0.02, size=width).astype(np.float32)
+    return Linear(K, hidden, width, code, r_in, rout, s_in, s_out)
+
+
+def _down_linear(ss: np.random.SeedSequence, K: int, inter: int, hidden: int, r_out, s_out) -> Linear:
+    """Down of one expert: children spawned in the order code, rin, s_in."""
+    c_code, c_rin, c_sin = ss.spawn(3)
+    code = _rng(c_code).integers(0, 1 << 16, size=(inter // 16, hidden // 16, 16 * K),
+                                 dtype=np.uint16).view(np.int16)
+    rin = _rng(c_rin).uniform(0.5, 1.5, size=inter).astype(np.float16)
+    s_in = _rng(c_sin).normal(1.0, 0.02, size=inter).astype(np.float32)
+    return Linear(K, inter, hidden, code, rin, r_out, s_in, s_out)
+
+
+def moe_mlp_layer(seed: int = 0, n_experts: int = N_EXPERTS, hidden: int = HIDDEN_MOE,
+                  inter: int = INTER_MOE, halves: int = INTER_MOE // HALF,
+                  experts: Optional[List[int]] = None) -> MoEMLPLayer:
+    """Draw a routed-expert MLP layer.  Widths: K ~ choice({2,3,4}, p = .3/.5/.2) per
+    (expert, half) for gate/up and per expert for down.  ``experts`` limits which experts
+    get arrays (the children of every expert are spawned, so any subset is reproducible)."""
+    assert inter % (halves * 16) == 0
+    width = inter // halves
+    root = np.random.SeedSequence([seed, 0x4D4C50])
+    c_kgu, c_kd, c_hid, c_exp = root.spawn(4)
+    K_gu = _rng(c_kgu).choice(np.array(MOE_K_CHOICES, np.int32), size=(n_experts, halves), p=MOE_K_PROBS)
+    K_d = _rng(c_kd).choice(np.array(MOE_K_CHOICES, np.int32), size=n_experts, p=MOE_K_PROBS)
+    ch = c_hid.spawn(4)
+    r_hi = _rng(ch[0]).uniform(0.5, 1.5, size=hidden).astype(np.float16)
+    s_hi = _rng(ch[1]).normal(1.0, 0.02, size=hidden).astype(np.float32)
+    r_ho = _rng(ch[2]).uniform(0.5, 1.5, size=hidden).astype(np.float16)
+    s_ho = _rng(ch[3]).normal(1.0, 0.02, size=hidden).astype(np.float32)
+    per = c_exp.spawn(n_experts)
+    gate, up, down = [None] * n_experts, [None] * n_experts, [None] * n_experts
+    for e in (range(n_experts) if experts is None else experts):
+        cg, cu, cd = per[e].spawn(3)
+        gate[e] = [_half_linear(c, int(K_gu[e, h]), hidden, width, r_hi, s_hi) for h, c in enumerate(cg.spawn(halves))]
+        up[e] = [_half_linear(c, int(K_gu[e, h]), hidden, width, r_hi, s_hi) for h, c in enumerate(cu.spawn(halves))]
+        down[e] = _down_linear(cd, int(K_d[e]), inter, hidden, r_ho, s_ho)
+    return MoEMLPLayer(hidden, inter, halves, K_gu, K_d, gate, up, down, r_hi, s_hi, r_ho, s_ho)
+
+
+def moe_router_weights(seed: int, n_tokens: int, n_routed: int = N_ROUTED) -> np.ndarray:
+    """f32 [n_tokens, n_routed]: positive router weights summing to one per token
+    (a flat Dirichlet draw)."""
+    rng = _rng(np.random.SeedSequence([seed, 0x525754]))
+    return rng.dirichlet(np.ones(n_routed), size=n_tokens).astype(np.float32)
