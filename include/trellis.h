@@ -145,6 +145,42 @@ int trellis_moe_gemv(const trellis_linear *experts, int E, const int32_t *routed
                      const uint16_t *shared_r, const float *shared_s, int shared_side,
                      uint16_t *y, void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of workspace trellis_moe_mlp needs for n routed experts (0 for invalid sizes). */
+size_t trellis_moe_mlp_workspace_bytes(int hidden, int inter, int halves, int n);
+
+/* Routed-expert MLP of one token, fused:
+ *   for k in [0, n), e = routed[k]:
+ *     g_k = gate_e(x), u_k = up_e(x)                   [inter]
+ *     a_k = silu(g_k) * u_k      (elementwise; silu(z) = z / (1 + e^-z))
+ *   y = sum_k router_w[k] * down_e(a_k)                [hidden]
+ * where every product is the trellis_gemv definition with that matrix's vectors.
+ * ("EXLR8" page: the calibration paragraph defines the expert activation a; the
+ *  width-manifest paragraph stores gate/up per "half" of 128 intermediate channels with its
+ *  own width and down with one width per expert, reached through a pointer table re-read
+ *  every launch; the shared-rotation paragraph makes the hidden-side vectors one per layer,
+ *  so x is rotated once for every expert and, because the down outputs share sv, the
+ *  weighted sum is taken before a single output rotation.)
+ * gate_up : DEVICE table [E][2*halves]: entry e*2H + h is slice h of gate_e (hidden ->
+ *           inter/H, output channels h*inter/H ...), entry e*2H + H + h slice h of up_e.
+ *           halves = inter/128 gives the per-half layout, halves = 1 one width per matrix.
+ *           Input-side vectors of the entries are ignored (shared ones used).
+ * down    : DEVICE table [E] (inter -> hidden); output-side vectors ignored.
+ * routed  : DEVICE int32 [n], ids in [0, E).  router_w: DEVICE f32 [n].
+ * x       : fp16 [hidden].  r_hidden_in/s_hidden_in: the shared gate/up input vectors,
+ *           r_hidden_out/s_hidden_out: the shared down output vectors (s may be NULL).
+ * act     : optional fp16 out [n][inter] receiving a_k (NULL: kept in the workspace).
+ * y       : fp16 out [hidden]; n = 0 writes zeros.
+ * ws      : zero-initialised device workspace of >= trellis_moe_mlp_workspace_bytes()
+ *           bytes, 256-byte aligned; its first word is the error word.
+ * Two partial/finishing launch pairs are enqueued.  A routed id out of range or an entry
+ * with an invalid K contributes zero and sets the error word.  a_k is stored as fp16 and is
+ * the input of down_e. */
+int trellis_moe_mlp(const trellis_linear *gate_up, const trellis_linear *down, int E, int halves,
+                    const int32_t *routed, const float *router_w, int n, int hidden, int inter,
+                    const uint16_t *x, const uint16_t *r_hidden_in, const float *s_hidden_in,
+                    const uint16_t *r_hidden_out, const float *s_hidden_out, uint16_t *act,
+                    uint16_t *y, void *ws, size_t ws_bytes, void *stream);
+
 /* Host-side check of a HOST copy of an expert table: K, cb, sizes, alignment, non-NULL
  * pointers (rin/rout may be NULL on a side that will be shared).  Returns TRELLIS_OK or the
  * first failing status (with the entry index in trellis_last_error()). */

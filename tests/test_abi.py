@@ -124,3 +124,39 @@ def test_moe_validation_and_table(L):
     assert L.trellis_validate_table(table, 4, 6144, 2048, 0) == 0  # input side shared
     table[2].out_features = 4096
     assert L.trellis_validate_table(table, 4, 6144, 2048, 0) == EINVAL
+
+
+def test_moe_mlp_workspace_bytes(L):
+    f = L.trellis_moe_mlp_workspace_bytes
+    assert f(6144, 2048, 16, 8) > 8 * 2048 * 2
+    assert f(6144, 2048, 1, 8) > 8 * 2048 * 2
+    assert f(6144, 2048, 16, 0) == 256
+    assert f(100, 2048, 16, 8) == 0          # hidden not a multiple of 128
+    assert f(6144, 2048, 3, 8) == 0          # inter not a multiple of 128 * halves
+    assert f(6144, 2048, 0, 8) == 0
+    assert f(6144, 2048, 16, -1) == 0
+
+
+def _mlp_call(L, **kw):
+    a = dict(gate_up=0x10000, down=0x20000, E=4, halves=2, routed=0x30000, router_w=0x31000, n=2,
+             hidden=256, inter=256, x=0x40000, r_hi=0x50000, s_hi=0x51000, r_ho=0x52000, s_ho=0x53000,
+             act=None, y=0x60000, ws=0x70000, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.trellis_moe_mlp(a["gate_up"], a["down"], a["E"], a["halves"], a["routed"], a["router_w"], a["n"],
+                             a["hidden"], a["inter"], a["x"], a["r_hi"], a["s_hi"], a["r_ho"], a["s_ho"],
+                             a["act"], a["y"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(E=0), EINVAL), (dict(gate_up=None), EINVAL), (dict(down=None), EINVAL),
+    (dict(halves=0), EINVAL), (dict(n=-1), EINVAL), (dict(hidden=200), EINVAL),
+    (dict(inter=384), EINVAL),                      # 384 is not a multiple of 128 * 2
+    (dict(y=None), EINVAL), (dict(r_ho=None), EINVAL), (dict(routed=None), EINVAL),
+    (dict(router_w=None), EINVAL), (dict(x=None), EINVAL), (dict(r_hi=None), EINVAL),
+    (dict(router_w=0x31002), EALIGN), (dict(gate_up=0x10004), EALIGN), (dict(act=0x80001), EALIGN),
+    (dict(s_ho=0x53002), EALIGN),
+    (dict(ws_bytes=255), EWORKSPACE), (dict(ws=None), EWORKSPACE), (dict(ws=0x70010), EWORKSPACE),
+])
+def test_moe_mlp_validation(L, kw, status):
+    assert _mlp_call(L, **kw) == status, L.trellis_last_error()
+    assert L.trellis_last_error()

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libtrellis.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "trellis.h")
 
 TRELLIS_OP_GEMV, TRELLIS_OP_GEMM, TRELLIS_OP_MOE_GEMV = 0, 1, 2
+TRELLIS_OP_MOE_MLP = 100  # workspace-cache key only (the C ABI has a dedicated size call)
 STATUS = {0: "TRELLIS_OK", -1: "TRELLIS_EINVAL", -2: "TRELLIS_EALIGN", -3: "TRELLIS_EWORKSPACE",
           -4: "TRELLIS_EUNSUPPORTED", -5: "TRELLIS_EHIP"}
 
@@ -77,6 +78,11 @@ def lib() -> ctypes.CDLL:
             L.trellis_gemm.argtypes = [ctypes.POINTER(CLinear), vp, i32, vp, vp, sz, vp]
             L.trellis_moe_gemv.restype = i32
             L.trellis_moe_gemv.argtypes = [vp, i32, vp, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, sz, vp]
+            L.trellis_moe_mlp_workspace_bytes.restype = sz
+            L.trellis_moe_mlp_workspace_bytes.argtypes = [i32, i32, i32, i32]
+            L.trellis_moe_mlp.restype = i32
+            L.trellis_moe_mlp.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          sz, vp]
             L.trellis_validate_table.restype = i32
             L.trellis_validate_table.argtypes = [ctypes.POINTER(CLinear), i32, i32, i32, i32]
             _lib = L
@@ -305,3 +311,89 @@ def moe_error_word(device="cuda") -> int:
     key = (torch.device(device).index or 0, _stream(), TRELLIS_OP_MOE_GEMV)
     w = _ws.get(key)
     return 0 if w is None else int(w[:4].view(torch.int32).item())
+
+
+class MoEMLPTables:
+    """Device tables of a routed-expert MLP layer: gate/up slices [E][2H] (entry e*2H + h is
+    slice h of gate_e, e*2H + H + h slice h of up_e) and down [E]."""
+
+    def __init__(self, gate: Sequence[Sequence[TrellisLinear]], up: Sequence[Sequence[TrellisLinear]],
+                 down: Sequence[TrellisLinear], device="cuda"):
+        self.E = len(down)
+        self.halves = len(gate[0])
+        entries = []
+        for e in range(self.E):
+            if len(gate[e]) != self.halves or len(up[e]) != self.halves:
+                raise ValueError(f"expert {e}: every expert needs {self.halves} gate and up slices")
+            entries += list(gate[e]) + list(up[e])
+        self.gate_up = ExpertTable(entries, shared_side=0, device=device)
+        self.down = ExpertTable(down, shared_side=1, device=device)
+        self.hidden = self.gate_up.in_features
+        self.inter = self.gate_up.out_features * self.halves
+        if self.down.in_features != self.inter or self.down.out_features != self.hidden:
+            raise ValueError("down must map inter -> hidden")
+
+    @classmethod
+    def from_host(cls, layer, device="cuda") -> "MoEMLPTables":
+        """From a ``synth.MoEMLPLayer``; the shared hidden-side arrays are uploaded once and
+        every descriptor points at that one copy."""
+        t = lambda a: torch.from_numpy(a).to(device)
+        r_hi, s_hi = t(layer.r_hidden_in), t(layer.s_hidden_in)
+        r_ho, s_ho = t(layer.r_hidden_out), t(layer.s_hidden_out)
+        dev = lambda l, rin, s_in, rout, s_out: TrellisLinear(t(l.code), rin, rout, s_in, s_out, l.K)
+        E = len(layer.down)
+        gate = [[dev(l, r_hi, s_hi, t(l.rout), t(l.s_out)) for l in layer.gate[e]] for e in range(E)]
+        up = [[dev(l, r_hi, s_hi, t(l.rout), t(l.s_out)) for l in layer.up[e]] for e in range(E)]
+        down = [dev(layer.down[e], t(layer.down[e].rin), t(layer.down[e].s_in), r_ho, s_ho) for e in range(E)]
+        obj = cls(gate, up, down, device=device)
+        obj.r_hidden_in, obj.s_hidden_in, obj.r_hidden_out, obj.s_hidden_out = r_hi, s_hi, r_ho, s_ho
+        return obj
+
+    def workspace_bytes(self, n: int) -> int:
+        nb = lib().trellis_moe_mlp_workspace_bytes(self.hidden, self.inter, self.halves, n)
+        if nb == 0:
+            raise ValueError(f"invalid MLP sizes for n={n}")
+        return nb
+
+
+def trellis_moe_mlp(tables: MoEMLPTables, routed: torch.Tensor, router_w: torch.Tensor, x: torch.Tensor,
+                    r_hidden_in: torch.Tensor, s_hidden_in: Optional[torch.Tensor],
+                    r_hidden_out: torch.Tensor, s_hidden_out: Optional[torch.Tensor],
+                    out: Optional[torch.Tensor] = None, act: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """routed int32 [n], router_w f32 [n], x fp16 [hidden] -> y fp16 [hidden].
+    ``act``: optional fp16 [n, inter] receiving silu(gate x) * up x."""
+    _req(routed, torch.int32, "routed")
+    dev = routed.device
+    _req(router_w, torch.float32, "router_w", dev)
+    _req(x, torch.float16, "x", dev)
+    n = routed.numel()
+    if router_w.numel() != n:
+        raise ValueError("router_w must have one weight per routed expert")
+    if x.numel() != tables.hidden:
+        raise ValueError(f"x must have {tables.hidden} elements")
+    for name, v, dt in (("r_hidden_in", r_hidden_in, torch.float16), ("r_hidden_out", r_hidden_out, torch.float16),
+                        ("s_hidden_in", s_hidden_in, torch.float32), ("s_hidden_out", s_hidden_out, torch.float32)):
+        if v is not None:
+            _req(v, dt, name, dev)
+            if v.numel() != tables.hidden:
+                raise ValueError(f"{name} must have {tables.hidden} elements")
+    if out is None:
+        out = torch.empty(tables.hidden, dtype=torch.float16, device=dev)
+    else:
+        _req(out, torch.float16, "out", dev)
+    if act is not None:
+        _req(act, torch.float16, "act", dev)
+        if act.numel() != n * tables.inter:
+            raise ValueError(f"act must have n*inter = {n * tables.inter} elements")
+    nb = tables.workspace_bytes(n)
+    if ws is None:
+        ws = workspace(nb, dev, TRELLIS_OP_MOE_MLP)
+    elif ws.numel() < nb:
+        raise ValueError(f"workspace of {ws.numel()} bytes < {nb}")
+    _check(lib().trellis_moe_mlp(tables.gate_up.table.data_ptr(), tables.down.table.data_ptr(), tables.E,
+                                 tables.halves, routed.data_ptr(), router_w.data_ptr(), n, tables.hidden,
+                                 tables.inter, x.data_ptr(), _ptr(r_hidden_in), _ptr(s_hidden_in),
+                                 _ptr(r_hidden_out), _ptr(s_hidden_out), _ptr(act), out.data_ptr(),
+                                 ws.data_ptr(), ws.numel(), _stream()))
+    return out

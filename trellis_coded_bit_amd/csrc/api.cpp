@@ -187,6 +187,7 @@ int trellis_moe_gemv(const trellis_linear *experts, int E, const int32_t *routed
   memset(&a.single, 0, sizeof(a.single));
   a.table = experts;
   a.E = E;
+  a.group = 1;
   a.routed = routed;
   a.n_problems = n;
   a.in_features = in_features;
@@ -199,6 +200,56 @@ int trellis_moe_gemv(const trellis_linear *experts, int E, const int32_t *routed
   a.shared_s = shared_s;
   a.shared_side = shared_side;
   return hip_status(trellis::launch_gemv(a, ws, ws_bytes, as_stream(stream)), "trellis_moe_gemv launch");
+}
+
+size_t trellis_moe_mlp_workspace_bytes(int hidden, int inter, int halves, int n) {
+  if (hidden <= 0 || inter <= 0 || halves < 1 || n < 0 || hidden % 128 || inter % (128 * halves)) return 0;
+  if ((long long)n * (inter / 128) * (hidden / 128) >= (1LL << 30)) return 0;
+  return trellis::moe_mlp_workspace_bytes(hidden, inter, halves, n);
+}
+
+int trellis_moe_mlp(const trellis_linear *gate_up, const trellis_linear *down, int E, int halves,
+                    const int32_t *routed, const float *router_w, int n, int hidden, int inter,
+                    const uint16_t *x, const uint16_t *r_hidden_in, const float *s_hidden_in,
+                    const uint16_t *r_hidden_out, const float *s_hidden_out, uint16_t *act,
+                    uint16_t *y, void *ws, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  if (E <= 0 || !gate_up || !down) return fail(TRELLIS_EINVAL, "empty or NULL expert tables");
+  if (halves < 1) return fail(TRELLIS_EINVAL, "halves=%d < 1", halves);
+  if (n < 0) return fail(TRELLIS_EINVAL, "n=%d < 0", n);
+  if (hidden <= 0 || inter <= 0 || hidden % 128 || inter % (128 * halves))
+    return fail(TRELLIS_EINVAL, "hidden=%d must be a positive multiple of 128 and inter=%d of 128*halves",
+                hidden, inter);
+  if ((long long)n * (inter / 128) * (hidden / 128) >= (1LL << 30))
+    return fail(TRELLIS_EINVAL, "n=%d routed experts of %dx%d exceed the work limit", n, hidden, inter);
+  if (!y || !r_hidden_out) return fail(TRELLIS_EINVAL, "y or r_hidden_out is NULL");
+  if (n > 0 && (!routed || !router_w || !x || !r_hidden_in))
+    return fail(TRELLIS_EINVAL, "routed, router_w, x or r_hidden_in is NULL");
+  if (!aligned(gate_up, 8) || !aligned(down, 8) || !aligned(routed, 4) || !aligned(router_w, 4) ||
+      !aligned(x, 2) || !aligned(y, 2) || !aligned(act, 2) || !aligned(r_hidden_in, 2) ||
+      !aligned(r_hidden_out, 2) || !aligned(s_hidden_in, 4) || !aligned(s_hidden_out, 4))
+    return fail(TRELLIS_EALIGN, "misaligned table, vector or buffer");
+  const size_t need = trellis::moe_mlp_workspace_bytes(hidden, inter, halves, n);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(TRELLIS_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+  trellis::MlpLaunch m{};
+  m.gate_up = gate_up;
+  m.down = down;
+  m.E = E;
+  m.halves = halves;
+  m.n = n;
+  m.hidden = hidden;
+  m.inter = inter;
+  m.routed = routed;
+  m.router_w = router_w;
+  m.x = x;
+  m.r_hidden_in = r_hidden_in;
+  m.s_hidden_in = s_hidden_in;
+  m.r_hidden_out = r_hidden_out;
+  m.s_hidden_out = s_hidden_out;
+  m.act = act;
+  m.y = y;
+  return hip_status(trellis::launch_moe_mlp(m, ws, ws_bytes, as_stream(stream)), "trellis_moe_mlp launch");
 }
 
 int trellis_validate_table(const trellis_linear *host_table, int E, int in_features,

@@ -98,9 +98,11 @@ __device__ __forceinline__ Problem get_problem(const GemvParams &P, int p) {
   trellis_linear d = P.L.single;
   bool ok = true;
   if (TABLE && P.L.table) {
-    const int e = P.L.routed[p];
+    const int grp = P.L.group;
+    const int slot = grp == 1 ? p : p / grp;
+    const int e = P.L.routed[slot];
     if (e < 0 || e >= P.L.E) ok = false;
-    else d = P.L.table[e];
+    else d = P.L.table[e * grp + (p - slot * grp)];
   }
   Problem r;
   r.code = reinterpret_cast<const uint32_t *>(d.code);
@@ -539,6 +541,99 @@ __global__ __launch_bounds__(kThreads) void gemv_finish_kernel(GemvParams P) {
   }
 }
 
+// Batch row 0 of column block q, column c: the contributors' partials added in workgroup
+// order (the order gemv_finish_kernel uses).
+__device__ __forceinline__ float partial_sum_b1(const GemvParams &P, int q, int c) {
+  const int g_lo = owner(q * P.nI, P.U, P.G), g_hi = owner((q + 1) * P.nI - 1, P.U, P.G);
+  const int seg_lo = q - wg_start(g_lo, P.U, P.G) / P.nI;
+  float v = 0.f;
+  for (int gb = g_lo; gb <= g_hi; gb += kPartialBatch) {
+    float part[kPartialBatch];
+#pragma unroll
+    for (int t = 0; t < kPartialBatch; ++t) {
+      const int gg = gb + t;
+      const size_t sl = (size_t)gg * P.maxseg + (gg == g_lo ? seg_lo : 0);
+      part[t] = gg <= g_hi ? P.partials[sl * kMaxB * 128 + c] : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < kPartialBatch; ++t) v += part[t];
+  }
+  return v;
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^-z) ("EXLR8" page, calibration paragraph: the
+// expert's down projection reads silu(gate x) * up x).  For z below about -88 e^-z is
+// +inf in fp32 and the quotient is -0, the limit.
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// kFinishSwiGLU, B = 1.  Workgroup f handles output block J of slice h of routed slot k
+// (f = (k*H + h)*nJ + J): threads 0..127 sum the gate entry's partials, threads 128..255
+// the up entry's; waves 0 and 2 rotate and scale them; then a = silu(g) * u is written as
+// fp16 to y[k][(h*nJ + J)*128 + c].
+__global__ __launch_bounds__(kThreads) void gemv_finish_swiglu_kernel(GemvParams P) {
+  __shared__ float gu[2][128];
+  const int H = P.L.halves, nJ = P.nJ;
+  const int f = blockIdx.x;
+  const int slot = f / (H * nJ), rem = f - slot * H * nJ;
+  const int pg = slot * 2 * H + rem / nJ, J = rem - (rem / nJ) * nJ;
+  const int tid = threadIdx.x, c = tid & 127, which = tid >> 7, lane = tid & 63;
+  const int p = which ? pg + H : pg;
+  const float v = partial_sum_b1(P, p * nJ + J, c);
+  const bool rot = (tid & 127) < 64;  // waves 0 (gate) and 2 (up)
+  float sa = 0.f, sb = 0.f;
+  if (rot) {
+    const Problem pr = get_problem(P, p);
+    if (pr.ok) {
+      const int c0 = J * 128 + lane, c1 = c0 + 64;
+      sa = h2f(ldg(pr.rout + c0)) * (1.0f / 128.0f);
+      sb = h2f(ldg(pr.rout + c1)) * (1.0f / 128.0f);
+      if (pr.s_out) { sa *= ldg(pr.s_out + c0); sb *= ldg(pr.s_out + c1); }
+    }
+  }
+  gu[which][c] = v;
+  __syncthreads();
+  if (rot) {
+    float va = gu[which][lane], vb = gu[which][lane + 64];
+    wave_fwht128(va, vb);
+    gu[which][lane] = va * sa;  // (an invalid entry has sa = sb = 0: its output is zero)
+    gu[which][lane + 64] = vb * sb;
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const int inter = H * nJ * 128;
+    P.L.y[(size_t)slot * inter + rem * 128 + c] = f2h(silu(gu[0][c]) * gu[1][c]);
+  }
+}
+
+// kFinishWeighted, B = 1.  Workgroup J: thread (r, c) (r = tid / 128, 8 of them) adds
+// w[k] * (sum of problem k's partials of block J) over k = r, r + 8, ..., in that order;
+// the eight sums are then added in r order, rotated once and scaled by the shared sv.
+constexpr int kWeightedThreads = 1024;
+__global__ __launch_bounds__(kWeightedThreads) void gemv_finish_weighted_kernel(GemvParams P) {
+  __shared__ float red[kWeightedThreads / 128][128];
+  const int tid = threadIdx.x, c = tid & 127, r = tid >> 7, lane = tid & 63;
+  const int J = blockIdx.x, nJ = P.nJ, n = P.L.n_problems;
+  float acc = 0.f;
+  for (int k = r; k < n; k += kWeightedThreads / 128) acc += ldg(P.L.router_w + k) * partial_sum_b1(P, k * nJ + J, c);
+  red[r][c] = acc;
+  __syncthreads();
+  if (tid < 64) {
+    float va = 0.f, vb = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWeightedThreads / 128; ++i) {
+      va += red[i][lane];
+      vb += red[i][lane + 64];
+    }
+    const int c0 = J * 128 + lane, c1 = c0 + 64;
+    float sa = h2f(ldg(P.L.shared_r + c0)) * (1.0f / 128.0f);
+    float sb = h2f(ldg(P.L.shared_r + c1)) * (1.0f / 128.0f);
+    if (P.L.shared_s) { sa *= ldg(P.L.shared_s + c0); sb *= ldg(P.L.shared_s + c1); }
+    wave_fwht128(va, vb);
+    P.L.y[c0] = f2h(va * sa);
+    P.L.y[c1] = f2h(vb * sb);
+  }
+}
+
 struct DeviceInfo {
   int cus = 0;
   int occ[kMaxB + 1] = {};
@@ -610,19 +705,34 @@ size_t gemv_workspace_bytes(int n_problems, int in_features, int out_features, i
   return geometry(n_problems, in_features, out_features, B).bytes;
 }
 
-hipError_t launch_gemv(const GemvLaunch &a, void *ws, size_t ws_bytes, hipStream_t stream) {
-  if (a.n_problems <= 0) return hipSuccess;
+namespace {
+
+// The partial and finishing launches of one problem list, with the error word and the
+// partials region given separately (the routed MLP places two lists in one workspace).
+hipError_t launch_gemv_parts(const GemvLaunch &a, uint32_t *errword, float *partials, size_t partial_bytes,
+                             hipStream_t stream) {
   if (a.B < 1 || a.B > kMaxB) return hipErrorInvalidValue;
+  if (a.finish != kFinishPlain && a.B != 1) return hipErrorInvalidValue;
+  if (a.n_problems <= 0) {
+    if (a.finish != kFinishWeighted) return hipSuccess;
+    // an empty weighted sum: y = 0 (the finishing kernel reads no partials)
+    GemvParams P{};
+    P.L = a;
+    P.L.n_problems = 0;
+    P.nJ = a.out_features / 128;
+    gemv_finish_weighted_kernel<<<P.nJ, kWeightedThreads, 0, stream>>>(P);
+    return hipGetLastError();
+  }
   const long long units = (long long)a.n_problems * (a.out_features / 128) * (a.in_features / 128);
   if (units >= (1LL << 31)) return hipErrorInvalidValue;
   const Geometry gm = geometry(a.n_problems, a.in_features, a.out_features, a.B);
-  if (ws_bytes < gm.bytes) return hipErrorInvalidValue;
+  if (partial_bytes < gm.bytes - gm.partials_off) return hipErrorInvalidValue;
   if ((long long)gm.G * gm.U >= (1LL << 32)) return hipErrorInvalidValue;  // 32-bit slot arithmetic
   GemvParams P;
   P.L = a;
-  char *w = static_cast<char *>(ws);
-  P.errword = reinterpret_cast<uint32_t *>(w);
-  P.partials = reinterpret_cast<float *>(w + gm.partials_off);
+  if (P.L.group < 1) P.L.group = 1;
+  P.errword = errword;
+  P.partials = partials;
   P.U = gm.U;
   P.G = gm.G;
   P.nI = gm.nI;
@@ -636,8 +746,84 @@ hipError_t launch_gemv(const GemvLaunch &a, void *ws, size_t ws_bytes, hipStream
   else gemv_partial_kernel<0><<<gm.G, kThreads, lds, stream>>>(P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  gemv_finish_kernel<<<gm.nq, kThreads, 0, stream>>>(P);
+  if (a.finish == kFinishSwiGLU) gemv_finish_swiglu_kernel<<<gm.nq / 2, kThreads, 0, stream>>>(P);
+  else if (a.finish == kFinishWeighted) gemv_finish_weighted_kernel<<<gm.nJ, kWeightedThreads, 0, stream>>>(P);
+  else gemv_finish_kernel<<<gm.nq, kThreads, 0, stream>>>(P);
   return hipGetLastError();
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+hipError_t launch_gemv(const GemvLaunch &a, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (a.n_problems <= 0 && a.finish != kFinishWeighted) return hipSuccess;
+  const size_t need = gemv_workspace_bytes(a.n_problems, a.in_features, a.out_features, a.B);
+  if (ws_bytes < need) return hipErrorInvalidValue;
+  char *w = static_cast<char *>(ws);
+  return launch_gemv_parts(a, reinterpret_cast<uint32_t *>(w), reinterpret_cast<float *>(w + 256), ws_bytes - 256,
+                           stream);
+}
+
+// Workspace of the routed MLP: [error word: 256 B][activations fp16 [n][inter], 256-aligned]
+// [partials: the larger of the two launches' regions].  The down launch reuses the gate/up
+// partials region: it runs after the gate/up finishing kernel on the same stream.
+size_t moe_mlp_workspace_bytes(int hidden, int inter, int halves, int n) {
+  if (n <= 0) return 256;
+  const size_t gu = gemv_workspace_bytes(n * 2 * halves, hidden, inter / halves, 1) - 256;
+  const size_t d = gemv_workspace_bytes(n, inter, hidden, 1) - 256;
+  return 256 + align256((size_t)n * inter * 2) + (gu > d ? gu : d);
+}
+
+hipError_t launch_moe_mlp(const MlpLaunch &m, void *ws, size_t ws_bytes, hipStream_t stream) {
+  const size_t need = moe_mlp_workspace_bytes(m.hidden, m.inter, m.halves, m.n);
+  if (ws_bytes < need) return hipErrorInvalidValue;
+  char *w = static_cast<char *>(ws);
+  uint32_t *errword = reinterpret_cast<uint32_t *>(w);
+  const size_t act_bytes = m.n > 0 ? align256((size_t)m.n * m.inter * 2) : 0;
+  uint16_t *act = m.act ? m.act : reinterpret_cast<uint16_t *>(w + 256);
+  float *partials = reinterpret_cast<float *>(w + 256 + act_bytes);
+  const size_t partial_bytes = ws_bytes - 256 - act_bytes;
+
+  GemvLaunch gu{};
+  gu.table = m.gate_up;
+  gu.E = m.E;
+  gu.group = 2 * m.halves;
+  gu.routed = m.routed;
+  gu.n_problems = m.n * 2 * m.halves;
+  gu.in_features = m.hidden;
+  gu.out_features = m.inter / m.halves;
+  gu.B = 1;
+  gu.x = m.x;
+  gu.x_per_problem = 0;
+  gu.y = act;
+  gu.shared_r = m.r_hidden_in;
+  gu.shared_s = m.s_hidden_in;
+  gu.shared_side = 0;
+  gu.finish = kFinishSwiGLU;
+  gu.halves = m.halves;
+  if (m.n > 0) {
+    const hipError_t e = launch_gemv_parts(gu, errword, partials, partial_bytes, stream);
+    if (e != hipSuccess) return e;
+  }
+  GemvLaunch d{};
+  d.table = m.down;
+  d.E = m.E;
+  d.group = 1;
+  d.routed = m.routed;
+  d.n_problems = m.n;
+  d.in_features = m.inter;
+  d.out_features = m.hidden;
+  d.B = 1;
+  d.x = act;
+  d.x_per_problem = 1;
+  d.y = m.y;
+  d.shared_r = m.r_hidden_out;
+  d.shared_s = m.s_hidden_out;
+  d.shared_side = 1;
+  d.finish = kFinishWeighted;
+  d.router_w = m.router_w;
+  return launch_gemv_parts(d, errword, partials, partial_bytes, stream);
 }
 
 }  // namespace trellis

@@ -19,13 +19,23 @@ hipError_t launch_had128(const void *x, int x_is_fp32, int rows, int n, const ui
                          const float *s, int post, float norm, void *y, int y_is_fp32,
                          hipStream_t stream);
 
-// One product problem list: either a single layer (table == NULL) or `n` routed entries of
-// a device table.
+// How the finishing launch combines the column blocks of a GEMV problem list.
+enum GemvFinish {
+  kFinishPlain = 0,     // y[p] = had(y_pre[p]) * sv_p for every problem p
+  kFinishSwiGLU = 1,    // problems in slots of 2H (H gate entries, then H up entries):
+                        // y[slot][h-th slice] = silu(gate_h) * up_h   (B = 1)
+  kFinishWeighted = 2,  // y = had(sum_p w[p] * y_pre[p]) * sv, sv shared   (B = 1)
+};
+
+// One product problem list: either a single layer (table == NULL) or the routed entries of
+// a device table.  With `group` entries per expert, problem p uses table entry
+// routed[p / group] * group + p % group.
 struct GemvLaunch {
   trellis_linear single;         // used when table == NULL
-  const trellis_linear *table;   // device table or NULL
-  int E;
-  const int32_t *routed;         // device [n] (table mode)
+  const trellis_linear *table;   // device table [E * group] or NULL
+  int E;                         // experts (valid routed ids are 0..E-1)
+  int group;                     // table entries per expert (>= 1)
+  const int32_t *routed;         // device [n_problems / group] (table mode)
   int n_problems;
   int in_features, out_features, B;
   const uint16_t *x;
@@ -34,6 +44,9 @@ struct GemvLaunch {
   const uint16_t *shared_r;
   const float *shared_s;
   int shared_side;
+  int finish;                    // GemvFinish
+  int halves;                    // kFinishSwiGLU: H
+  const float *router_w;         // kFinishWeighted: device f32 [n_problems]
 };
 
 // Workspace bytes for a GEMV launch with n_problems problems of [in, out] at batch B.
@@ -41,6 +54,22 @@ size_t gemv_workspace_bytes(int n_problems, int in_features, int out_features, i
 // Upper bound on n_problems * out_features / 128 for one GEMV/MoE call.
 int gemv_max_column_blocks();
 hipError_t launch_gemv(const GemvLaunch &a, void *ws, size_t ws_bytes, hipStream_t stream);
+
+// Routed-expert MLP of one token: gate/up halves (table [E][2H]) -> silu(g)*u -> down
+// (table [E]) -> router-weighted sum with one output rotation.
+struct MlpLaunch {
+  const trellis_linear *gate_up, *down;
+  int E, halves, n, hidden, inter;
+  const int32_t *routed;
+  const float *router_w;
+  const uint16_t *x;
+  const uint16_t *r_hidden_in, *r_hidden_out;
+  const float *s_hidden_in, *s_hidden_out;
+  uint16_t *act;  // fp16 [n][inter] or NULL (then held in the workspace)
+  uint16_t *y;
+};
+size_t moe_mlp_workspace_bytes(int hidden, int inter, int halves, int n);
+hipError_t launch_moe_mlp(const MlpLaunch &m, void *ws, size_t ws_bytes, hipStream_t stream);
 
 size_t gemm_workspace_bytes(int in_features, int out_features, int M);
 hipError_t launch_gemm(const trellis_linear &L, const uint16_t *x, int M, uint16_t *y, void *ws,

@@ -230,22 +230,25 @@ class MoEMLPLayer:
 
 
 def _half_linear(ss: np.random.SeedSequence, K: int, hidden: int, width: int, r_in, s_in) -> Linear:
-    """One gate/up half: children spawned in the order code, rout, s_out."""
+    """One gate/up half: children spawned in the order code, rout, s_out.  s_out is drawn
+    from N(1, 0.02) / sqrt(hidden): the projection's global scale (the EXLR8 page folds one
+    per projection into the stored side vectors) keeps outputs of order one."""
     c_code, c_rout, c_sout = ss.spawn(3)
     code = _rng(c_code).integers(0, 1 << 16, size=(hidden // 16, width // 16, 16 * K),
                                  dtype=np.uint16).view(np.int16)
     rout = _rng(c_rout).uniform(0.5, 1.5, size=width).astype(np.float16)
-    s_out = _rng(c_sout).normal(1.0, 0.02, size=width).astype(np.float32)
+    s_out = (_rng(c_sout).normal(1.0, 0.02, size=width) / np.sqrt(hidden)).astype(np.float32)
     return Linear(K, hidden, width, code, r_in, rout, s_in, s_out)
 
 
 def _down_linear(ss: np.random.SeedSequence, K: int, inter: int, hidden: int, r_out, s_out) -> Linear:
-    """Down of one expert: children spawned in the order code, rin, s_in."""
+    """Down of one expert: children spawned in the order code, rin, s_in; s_in is drawn from
+    N(1, 0.02) / sqrt(inter) (the global scale, as for gate/up)."""
     c_code, c_rin, c_sin = ss.spawn(3)
     code = _rng(c_code).integers(0, 1 << 16, size=(inter // 16, hidden // 16, 16 * K),
                                  dtype=np.uint16).view(np.int16)
     rin = _rng(c_rin).uniform(0.5, 1.5, size=inter).astype(np.float16)
-    s_in = _rng(c_sin).normal(1.0, 0.02, size=inter).astype(np.float32)
+    s_in = (_rng(c_sin).normal(1.0, 0.02, size=inter) / np.sqrt(inter)).astype(np.float32)
     return Linear(K, inter, hidden, code, rin, r_out, s_in, s_out)
 
 
