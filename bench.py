@@ -7,8 +7,8 @@ Metric: code bytes (in*out*K/8 summed over the three matrices) per second.
 Weights are rotated over enough distinct device copies (> 1 GiB in total) that the 256 MB
 Infinity Cache cannot serve them between steps; inputs are resident in HBM before timing.
 
-Prints ONE JSON line (rank 0, N = 1).  Extra workloads (small-batch, MoE, prefill) are
-available with --workload for separate measurement lines.
+Prints ONE JSON line (rank 0, N = 1).  Extra workloads (small-batch, MoE, the fused
+routed-expert MLP, prefill) are available with --workload for separate measurement lines.
 """
 from __future__ import annotations
 
@@ -367,15 +367,88 @@ def run_moe(args, torch, tb, synth):
             "code_bytes_per_token": nb, "code_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
 
 
+def run_moe_mlp(args, torch, tb, synth):
+    """The fused routed-expert MLP of one token (trellis_moe_mlp): gate/up over 16 per-half
+    slices of each of the 8 routed experts, silu(g) * u, down, router-weighted sum with one
+    output rotation.  Routes and router weights re-drawn every token over 256 experts.  The
+    same token computed with the unfused calls (two trellis_moe_gemv launches, the
+    activation and the weighted sum as torch ops) is timed beside it."""
+    layer = synth.moe_mlp_layer(args.seed)
+    E, H = len(layer.down), layer.halves
+    tables = tb.MoEMLPTables.from_host(layer)
+    n_tok = args.warmup + args.steps + 64
+    routes = synth.moe_routes(args.seed, n_tok)
+    weights = synth.moe_router_weights(args.seed, n_tok)
+    r_dev = torch.from_numpy(routes).cuda()
+    w_dev = torch.from_numpy(weights).cuda()
+    x = torch.from_numpy(synth.make_x(np.random.SeedSequence([args.seed, 0x4D4C58]), 1, layer.hidden)[0]).cuda()
+    y = torch.empty(layer.hidden, dtype=torch.float16, device="cuda")
+    ws = torch.zeros(tables.workspace_bytes(8), dtype=torch.uint8, device="cuda")
+    bytes_tok = [sum(layer.expert_code_bytes(int(e)) for e in r) for r in routes]
+
+    def step(i):
+        tb.trellis_moe_mlp(tables, r_dev[i], w_dev[i], x, tables.r_hidden_in, tables.s_hidden_in,
+                           tables.r_hidden_out, tables.s_hidden_out, out=y, ws=ws)
+
+    # unfused: the same products through trellis_moe_gemv (gate/up slices of the routed
+    # experts as one problem list), the activation and the weighted sum in torch
+    slots = torch.arange(2 * H, dtype=torch.int32, device="cuda")
+    routes_gu = (r_dev[:, :, None] * (2 * H) + slots[None, None, :]).reshape(n_tok, -1).contiguous()
+    y_gu = torch.empty((8 * 2 * H, layer.inter // H), dtype=torch.float16, device="cuda")
+    act = torch.empty((8, layer.inter), dtype=torch.float16, device="cuda")
+    y_d = torch.empty((8, layer.hidden), dtype=torch.float16, device="cuda")
+    ws_u = torch.zeros(max(tables.gate_up.workspace_bytes(16 * H), tables.down.workspace_bytes(8)),
+                       dtype=torch.uint8, device="cuda")
+
+    def step_unfused(i):
+        tb.trellis_moe_gemv(tables.gate_up, routes_gu[i], x, False, tables.r_hidden_in, tables.s_hidden_in, 0,
+                            out=y_gu, ws=ws_u)
+        g = y_gu.view(8, 2, layer.inter).float()
+        torch.mul(torch.nn.functional.silu(g[:, 0]), g[:, 1], out=act)
+        tb.trellis_moe_gemv(tables.down, r_dev[i], act, True, tables.r_hidden_out, tables.s_hidden_out, 1,
+                            out=y_d, ws=ws_u)
+        torch.mm(w_dev[i][None, :].half(), y_d, out=y.view(1, -1))
+
+    res = {}
+    variants = (("fused", step),) if args.no_unfused else (("fused", step), ("unfused", step_unfused))
+    for name, fn in variants:
+        for i in range(64):  # warm-up tokens route across most of the 256 experts
+            fn(i)
+        torch.cuda.synchronize()
+        chunk = 16
+        n_chunks = max(1, args.steps // chunk)
+        graphs = [_capture(torch, lambda c=c: [fn(64 + c * chunk + j) for j in range(chunk)]) for c in range(n_chunks)]
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for g in graphs:
+            g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        res[name] = s.elapsed_time(e) / (n_chunks * chunk)
+        del graphs
+    steps = n_chunks * chunk
+    nb = float(np.mean(bytes_tok[64:64 + steps]))
+    ms = res["fused"]
+    return {"workload": "fused routed-expert MLP decode (trellis_moe_mlp), 8 of 256 GLM-like experts, hidden 6144, "
+                        "intermediate 2048 as 16 gate/up halves per expert with per-half K in {2,3,4}, down K per "
+                        "expert; routes and router weights re-drawn every token; 16 tokens per HIP graph",
+            "ms_per_token": round(ms, 5), "code_bytes_per_token": nb, "code_GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "unfused_ms_per_token": round(res["unfused"], 5) if "unfused" in res else None, "tokens_timed": steps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--workload", default="dense", choices=["dense", "small_batch", "moe", "prefill"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "small_batch", "moe", "moe_mlp", "prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true", help="moe_mlp: time only the fused call")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -404,6 +477,8 @@ def main():
             print(json.dumps(run_small_batch(args, torch, tb, synth, B)), flush=True)
     elif args.workload == "moe":
         print(json.dumps(run_moe(args, torch, tb, synth)), flush=True)
+    elif args.workload == "moe_mlp":
+        print(json.dumps(run_moe_mlp(args, torch, tb, synth)), flush=True)
     else:
         print(json.dumps(run_prefill(args, torch, tb, synth)), flush=True)
 
