@@ -10,10 +10,10 @@ Sources (cited by page title and section; no line numbers):
   the tile / tensor-core permutation paragraph and the Shannon-bound paragraph.
 * [EXLR8]  the EXLR8 format page -- the rotation paragraphs (Q = signs x Hadamard), the
   tile-coding paragraph (Viterbi over a 16-bit-state trellis), the shared hidden-side
-  rotation paragraph, the calibration paragraph (the expert MLP's activation) and the
-  width-manifest paragraph (per-half widths).
+  rotation paragraph, the calibration paragraph (the expert MLP's activation), the
+  width-manifest paragraph (per-half widths) and the E4M3 paragraph (the FP8 codebook).
 
-Readings taken where the pages are silent or disagree are named A1..A21 in the
+Readings taken where the pages are silent or disagree are named A1..A25 in the
 docstrings and listed in the design notes.  Every function here follows the plain
 definition; nothing is blocked, fused or reordered beyond what the definition states.
 """
@@ -130,6 +130,68 @@ def codebook_table() -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------------
+# E4M3 (the FP8 codebook variant)
+# ----------------------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_magnitudes() -> np.ndarray:
+    """Values of the codes 0..126 (sign bit clear), float64, increasing.
+
+    OCP 8-bit floating point, E4M3 flavour: 1 sign, 4 exponent (bias 7), 3 mantissa bits;
+    exponent field 0 holds subnormals m/8 * 2^-6; code 0x7F is NaN and there are no
+    infinities, so the largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    out = []
+    for code in range(127):
+        e, m = code >> 3, code & 7
+        out.append((m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(out)
+
+
+def e4m3_codes(v) -> np.ndarray:
+    """Round to E4M3: nearest finite value, ties to the even code, saturating at +-448.
+    Returns uint8 codes (sign in bit 7; a negative value that rounds to zero keeps its sign).
+
+    [EXLR8] E4M3 paragraph: every codebook value is rounded to E4M3 with round-to-nearest-
+    even and saturation.  Written out from the definition: the two neighbouring
+    representable magnitudes are found and the nearer taken; on a tie the one whose code
+    is even.  NaN inputs are outside the domain.
+    """
+    v = np.asarray(v, np.float64)
+    mags = e4m3_magnitudes()
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 126)  # first magnitude >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return code | np.where(np.signbit(v), np.uint8(0x80), np.uint8(0))
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """E4M3 codes (uint8, no NaN code) -> float64."""
+    c = np.asarray(codes, np.uint8)
+    mag = e4m3_magnitudes()[c & 0x7F]
+    return np.where(c & 0x80, -mag, mag)
+
+
+def e4m3_round(v) -> np.ndarray:
+    return e4m3_value(e4m3_codes(v))
+
+
+def codebook_e4m3(states: np.ndarray) -> np.ndarray:
+    """E4M3 codebook code of each state (uint8): the fp16 codebook value rounded to E4M3.
+
+    [EXLR8] E4M3 paragraph (decoding is EXL3's algorithm followed by the E4M3 rounding);
+    reading A19: the rounding applies to the fp16 value codebook() produces.  Every
+    codebook magnitude is below 3.96 (rounding to at most 4), so saturation never acts here.
+    """
+    return e4m3_codes(codebook(states).astype(np.float64))
+
+
+# ----------------------------------------------------------------------------------------
 # Tile permutation and placement
 # ----------------------------------------------------------------------------------------
 
@@ -166,13 +228,24 @@ def tiles_to_matrix(values: np.ndarray) -> np.ndarray:
     return tiles.transpose(0, 2, 1, 3).reshape(16 * Ti, 16 * Tj)
 
 
-def decode_tiles(code: np.ndarray, K: int) -> np.ndarray:
-    """Packed code int16 [in/16, out/16, 16K] -> W_hat float16 [in, out] (codebook domain)."""
+def decode_tiles(code: np.ndarray, K: int, cb: int = 1) -> np.ndarray:
+    """Packed code int16 [in/16, out/16, 16K] -> W_hat float16 [in, out] (codebook domain).
+
+    cb = 1: the MCG codebook's fp16 values; cb = 2: those values rounded to E4M3
+    (codebook_e4m3), returned as float16 (every E4M3 value is exactly representable).
+    """
     code = np.asarray(code)
     Ti, Tj, nw = code.shape
-    assert nw == 16 * K
-    vals = codebook(tile_states(code, K))
+    assert nw == 16 * K and cb in (1, 2)
+    st = tile_states(code, K)
+    vals = codebook(st) if cb == 1 else e4m3_value(codebook_e4m3(st)).astype(np.float16)
     return tiles_to_matrix(vals)
+
+
+def decode_tiles_e4m3(code: np.ndarray, K: int) -> np.ndarray:
+    """Packed code -> E4M3 codes uint8 [in, out] of the cb = 2 weights."""
+    code = np.asarray(code)
+    return tiles_to_matrix(codebook_e4m3(tile_states(code, K)))
 
 
 # ----------------------------------------------------------------------------------------
@@ -227,13 +300,21 @@ def side_scale(r: np.ndarray, s: Optional[np.ndarray]) -> np.ndarray:
 # ----------------------------------------------------------------------------------------
 
 def forward(code: np.ndarray, K: int, rin, rout, s_in, s_out, x: np.ndarray,
-            col_blocks: Optional[Sequence[int]] = None, row_chunk: int = 64) -> np.ndarray:
+            col_blocks: Optional[Sequence[int]] = None, row_chunk: int = 64, cb: int = 1,
+            act_e4m3: bool = False) -> np.ndarray:
     """y = had(had(x * su) @ W_hat) * sv, float64 [B, out] (or [B, 128*len(col_blocks)]).
 
     [METAL] reconstruction paragraph: xh = had_blockwise(x*su); y_pre = xh @ W_hat;
     y = had_blockwise(y_pre) * sv.  Reading A11: no bias.  W_hat is decoded in chunks of
     tile rows (memory only; the sum is the plain matrix product).  ``col_blocks`` restricts
     the output to the listed 128-column blocks, which needs only those blocks' tiles.
+    ``cb`` selects the codebook (decode_tiles).
+
+    act_e4m3 (the FP8 prefill of [EXLR8]: the E4M3 weights of cb = 2 feed FP8 matrix
+    multiplies, so the rotated activations are E4M3 too).  Reading A25: each row of xh is
+    quantised with its own scale sc = max|xh_row| / 448, q = e4m3_round(xh_row / sc)
+    (round to nearest even, saturating), and y_pre_row = sc * (q @ W_hat); an all-zero row
+    has q = 0.
     """
     code = np.asarray(code)
     Ti, Tj, _ = code.shape
@@ -243,6 +324,11 @@ def forward(code: np.ndarray, K: int, rin, rout, s_in, s_out, x: np.ndarray,
     su = side_scale(rin, s_in)
     sv = side_scale(rout, s_out)
     xh = had_blocks(x * su)
+    sc = np.ones(x.shape[0])
+    if act_e4m3:
+        amax = np.max(np.abs(xh), axis=1)
+        sc = amax / E4M3_MAX
+        xh = np.where(amax[:, None] > 0, e4m3_round(xh / np.where(amax > 0, sc, 1.0)[:, None]), 0.0)
     if col_blocks is None:
         cols = np.arange(Tj)
     else:
@@ -250,15 +336,17 @@ def forward(code: np.ndarray, K: int, rin, rout, s_in, s_out, x: np.ndarray,
     sub = code[:, cols, :]
     y_pre = np.zeros((x.shape[0], 16 * len(cols)))
     for a in range(0, Ti, row_chunk):
-        w = decode_tiles(sub[a:a + row_chunk], K).astype(np.float64)
+        w = decode_tiles(sub[a:a + row_chunk], K, cb).astype(np.float64)
         y_pre += xh[:, 16 * a:16 * a + w.shape[0]] @ w
+    y_pre *= sc[:, None]
     ch = np.concatenate([np.arange(16 * j, 16 * j + 16) for j in cols])
     return had_blocks(y_pre) * sv[ch]
 
 
-def forward_linear(lin, x, col_blocks=None) -> np.ndarray:
-    """forward() on a ``synth.Linear``-like object."""
-    return forward(lin.code, lin.K, lin.rin, lin.rout, lin.s_in, lin.s_out, x, col_blocks)
+def forward_linear(lin, x, col_blocks=None, act_e4m3: bool = False) -> np.ndarray:
+    """forward() on a ``synth.Linear``-like object (its ``cb``, default 1)."""
+    return forward(lin.code, lin.K, lin.rin, lin.rout, lin.s_in, lin.s_out, x, col_blocks,
+                   cb=getattr(lin, "cb", 1), act_e4m3=act_e4m3)
 
 
 def dense_weight(code: np.ndarray, K: int, rin, rout, s_in, s_out) -> np.ndarray:

@@ -323,6 +323,106 @@ def test_shannon_band_catches_offset_decode():
 
 
 # ---------------------------------------------------------------------------------------
+# E4M3 codebook and FP8 prefill ([EXLR8] E4M3 paragraph)
+# ---------------------------------------------------------------------------------------
+
+def test_e4m3_hand_derived_values():
+    """From the OCP E4M3 definition (bias 7, 3 mantissa bits, subnormal step 2^-9, max 448):
+    ties go to the even code, values past 448 saturate, a negative value keeps its sign."""
+    cases = [
+        (1.0625, 1.0),          # halfway 1.0 (code 0x38, even) / 1.125 (0x39)
+        (1.1875, 1.25),         # halfway 1.125 (0x39) / 1.25 (0x3A, even)
+        (2.0 ** -10, 0.0),      # halfway 0 (even) / 2^-9 (code 1)
+        (3 * 2.0 ** -10, 2.0 ** -8),  # halfway 2^-9 (code 1) / 2^-8 (code 2, even)
+        (2.0 ** -6, 2.0 ** -6), # smallest normal, exact
+        (0.3, 0.3125),          # [0.25, 0.5) has step 1/32: 0.28125 / 0.3125, nearer the latter
+        (448.0, 448.0), (464.0, 448.0), (500.0, 448.0), (1e9, 448.0), (-500.0, -448.0),
+        (1.84375, 1.875),       # codebook value of the all-zero state
+        (0.85009765625, 0.875), # codebook value of state 0xFFFF
+    ]
+    for v, want in cases:
+        assert O.e4m3_round(v) == want, v
+    assert np.signbit(O.e4m3_round(-2.0 ** -11)) and O.e4m3_round(-2.0 ** -11) == 0.0
+    assert O.e4m3_codes(448.0) == 0x7E and O.e4m3_codes(-1.0) == 0xB8
+    m = O.e4m3_magnitudes()
+    assert len(m) == 127 and np.all(np.diff(m) > 0) and m[1] == 2.0 ** -9
+
+
+def test_e4m3_matches_library_cast_on_every_fp16():
+    """torch's float8_e4m3fn cast (round to nearest even) agrees on every finite fp16 value
+    of magnitude <= 448; above it torch does not saturate, so that range is checked by the
+    definition: everything from 448 up maps to 448."""
+    import torch
+    h = np.arange(1 << 16, dtype=np.uint16).view(np.float16).astype(np.float64)
+    fin = h[np.isfinite(h)]
+    inr = fin[np.abs(fin) <= 448]
+    ref = torch.from_numpy(inr).to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.e4m3_codes(inr), ref)
+    big = fin[np.abs(fin) > 448]
+    np.testing.assert_array_equal(O.e4m3_round(big), np.sign(big) * 448.0)
+
+
+def test_codebook_e4m3_table():
+    st = np.arange(1 << 16, dtype=np.uint32)
+    v16 = O.codebook(st).astype(np.float64)
+    v8 = O.e4m3_value(O.codebook_e4m3(st))
+    # every value is the E4M3 value nearest the fp16 one: within half a step of it
+    step = np.where(np.abs(v8) >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(v8), 2.0 ** -6))) - 3), 2.0 ** -9)
+    assert np.all(np.abs(v8 - v16) <= step / 2 + 1e-15)
+    assert np.all(np.abs(v8) <= 4) and np.max(np.abs(v8)) == 4.0  # |fp16 value| <= 3.9502 rounds up to 4
+    assert O.e4m3_value(O.codebook_e4m3(np.array([0], np.uint32)))[0] == 1.875
+    # decode of the cb=2 variant is the E4M3 rounding of the cb=1 decode, tile by tile
+    code = synth.make_linear(np.random.SeedSequence(31), 3, 64, 48).code
+    np.testing.assert_array_equal(O.decode_tiles(code, 3, cb=2).astype(np.float64),
+                                  O.e4m3_round(O.decode_tiles(code, 3).astype(np.float64)))
+    np.testing.assert_array_equal(O.e4m3_value(O.decode_tiles_e4m3(code, 3)),
+                                  O.decode_tiles(code, 3, cb=2).astype(np.float64))
+
+
+def test_fp8_prefill_one_hot_rotation():
+    """x chosen so that had(x*su) is the k-th unit vector: its row scale is 1/448, its code
+    is exactly 448 at k, and y must be had(row k of the E4M3 weights) * sv."""
+    lin = synth.make_linear(np.random.SeedSequence(32), 2, 256, 256)
+    lin.cb = 2
+    su = lin.rin.astype(np.float64) * lin.s_in
+    sv = lin.rout.astype(np.float64) * lin.s_out
+    H = scipy.linalg.hadamard(128) / math.sqrt(128)
+    for k in (0, 77, 200):
+        e = np.zeros(256)
+        e[k] = 1.0
+        x = (np.kron(np.eye(2), H) @ e) / su
+        y = O.forward_linear(lin, x[None, :], act_e4m3=True)[0]
+        w8 = O.decode_tiles(lin.code, 2, cb=2).astype(np.float64)
+        ref = (np.kron(np.eye(2), H) @ w8[k]) * sv
+        assert O.rel_l2(y, ref) < 1e-12, k
+    # two-hot: xh = e_3 + 0.6 e_150.  Row scale 1/448; 0.6 * 448 = 268.8 lies between the
+    # E4M3 values 256 and 288 (step 32 in [256, 448]) and rounds to 256, so y_pre =
+    # w8[3] + (256/448) w8[150].
+    e = np.zeros(256)
+    e[3], e[150] = 1.0, 0.6
+    x = (np.kron(np.eye(2), H) @ e) / su
+    y = O.forward_linear(lin, x[None, :], act_e4m3=True)[0]
+    ref = (np.kron(np.eye(2), H) @ (w8[3] + (256.0 / 448.0) * w8[150])) * sv
+    assert O.rel_l2(y, ref) < 1e-12
+
+
+def test_fp8_prefill_scaling_and_quantisation_band():
+    """Powers of two pass through the row scale exactly; a zero row gives zero; against the
+    unquantised cb=2 forward the activation rounding costs 1-5 % relative L2 (E4M3 keeps 3
+    mantissa bits: relative rounding error up to 2^-4 per element)."""
+    lin = synth.make_linear(np.random.SeedSequence(33), 3, 384, 256)
+    lin.cb = 2
+    x = synth.make_x(np.random.SeedSequence(34), 3, 384).astype(np.float64)
+    x[1] = 0.0
+    y = O.forward_linear(lin, x, act_e4m3=True)
+    np.testing.assert_allclose(O.forward_linear(lin, 8.0 * x, act_e4m3=True), 8.0 * y, rtol=1e-13, atol=0)
+    assert np.all(y[1] == 0)
+    exact = O.forward_linear(lin, x)
+    for r in (0, 2):
+        assert 0.005 < O.rel_l2(y[r], exact[r]) < 0.05
+
+
+# ---------------------------------------------------------------------------------------
 # Routed-expert MLP ([EXLR8] calibration and width-manifest paragraphs)
 # ---------------------------------------------------------------------------------------
 

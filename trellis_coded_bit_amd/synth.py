@@ -46,6 +46,7 @@ class Linear:
     rout: np.ndarray  # float16 [out]
     s_in: np.ndarray  # float32 [in]
     s_out: np.ndarray  # float32 [out]
+    cb: int = 1  # codebook: 1 = MCG fp16 values, 2 = the same rounded to E4M3
 
     @property
     def code_bytes(self) -> int:
