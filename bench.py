@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+MFMA_F8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 # Vector-ALU bound of the codebook decode: 1024 SIMDs at 2.4 GHz; per wave64 of 4 weights
 # per lane (256 weights) the hash needs 4 window extractions and 4 32-bit multiplies (half
 # lane rate: 4 clocks each) and 4 mask-xors (full rate: 2 clocks each) = 40 clocks.
@@ -249,25 +250,34 @@ def run_dense(args, torch, tb, synth):
     return out, wl
 
 
-def run_prefill(args, torch, tb, synth):
+def run_prefill(args, torch, tb, synth, fp8=False):
+    """trellis_gemm (fp16 matrix cores) or, with fp8, trellis_gemm_fp8 on the E4M3 variant
+    of the same codes (cb = 2; activations quantised per row to E4M3)."""
     wl = synth.prefill(args.seed)
     lin = wl.layers["w"]
     L = tb.TrellisLinear.from_host(lin)
+    if fp8:
+        L = tb.TrellisLinear(L.code, L.rin, L.rout, L.s_in, L.s_out, L.K, cb=2)
+    fn = tb.trellis_gemm_fp8 if fp8 else tb.trellis_gemm
     x = torch.from_numpy(wl.xs["w"]).cuda()
     y = torch.empty((x.shape[0], lin.out_features), dtype=torch.float16, device="cuda")
     for _ in range(max(10, args.warmup)):  # also lets the clocks settle under the MFMA load
-        tb.trellis_gemm(L, x, out=y)
+        fn(L, x, out=y)
     torch.cuda.synchronize()
     n = max(10, args.steps // 2)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(n):
-        tb.trellis_gemm(L, x, out=y)
+        fn(L, x, out=y)
     e.record()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / n
     flops = 2.0 * x.shape[0] * lin.in_features * lin.out_features
     tf = flops / (ms * 1e-3) / 1e12
+    if fp8:
+        return {"workload": "FP8 prefill (trellis_gemm_fp8): E4M3 codebook K3 5120x17408, M=2048, E4M3 activations "
+                            "with per-row scales", "ms": round(ms, 4), "tflops": round(tf, 1),
+                "frac_of_fp8_mfma_peak": round(tf / MFMA_F8_PEAK_TFLOPS, 4)}
     return {"workload": "prefill K3 5120x17408, M=2048", "ms": round(ms, 4), "tflops": round(tf, 1),
             "frac_of_fp16_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
 
@@ -467,6 +477,7 @@ def main():
         out, wl = run_dense(args, torch, tb, synth)
         if not args.no_prefill:
             out["prefill"] = run_prefill(args, torch, tb, synth)
+            out["prefill_fp8"] = run_prefill(args, torch, tb, synth, fp8=True)
         if args.copy_probe:
             out["copy_probe"] = copy_probe(torch)
         if not args.no_cpu_baseline:
@@ -481,6 +492,7 @@ def main():
         print(json.dumps(run_moe_mlp(args, torch, tb, synth)), flush=True)
     else:
         print(json.dumps(run_prefill(args, torch, tb, synth)), flush=True)
+        print(json.dumps(run_prefill(args, torch, tb, synth, fp8=True)), flush=True)
 
 
 if __name__ == "__main__":

@@ -58,9 +58,13 @@ typedef enum {
  * code  : int16 [in/16][out/16][16*K], 16-byte aligned.
  * rin   : fp16 [in]  (EXL3 suh);  rout: fp16 [out] (EXL3 svh).
  * s_in  : f32 [in]  or NULL (= all ones);  s_out: f32 [out] or NULL (= all ones).
- * K in {2,3,4}; cb must be 1 (the MCG codebook); in and out multiples of 128.
+ * K in {2,3,4}; in and out multiples of 128.
+ * cb = 1: the MCG codebook (fp16 values); cb = 2: the same values rounded to E4M3 (round to
+ * nearest, ties to even, saturating), the EXLR8 format's codebook.
  * ("The escha W2 format, recovered and verified", "Tensor mapping": the config tensor
- *  [16, bits, cb, 1, in, out] fixes tile 16, K = bits, cb.) */
+ *  [16, bits, cb, 1, in, out] fixes tile 16, K = bits, cb; "EXLR8" page, E4M3 paragraph.)
+ * trellis_gemv, trellis_gemm and the MoE calls take cb = 1 (cb = 2: TRELLIS_EUNSUPPORTED,
+ * or a zero row for a table entry); trellis_gemm_fp8 takes cb = 2. */
 typedef struct {
   const int16_t *code;
   const uint16_t *rin;
@@ -74,7 +78,7 @@ typedef struct {
 } trellis_linear;
 
 /* Operation ids for trellis_workspace_bytes(). */
-enum { TRELLIS_OP_GEMV = 0, TRELLIS_OP_GEMM = 1, TRELLIS_OP_MOE_GEMV = 2 };
+enum { TRELLIS_OP_GEMV = 0, TRELLIS_OP_GEMM = 1, TRELLIS_OP_MOE_GEMV = 2, TRELLIS_OP_GEMM_FP8 = 3 };
 
 int trellis_abi_version(void);
 
@@ -104,7 +108,7 @@ int had128_scale(const void *x, int x_is_fp32, int rows, int n, const uint16_t *
                  int post, void *y, int y_is_fp32, void *stream);
 
 /* Bytes of workspace needed by an op.  op = TRELLIS_OP_GEMV (batch_or_M = B),
- * TRELLIS_OP_GEMM (batch_or_M = M), TRELLIS_OP_MOE_GEMV (L = any entry of the uniform
+ * TRELLIS_OP_GEMM or TRELLIS_OP_GEMM_FP8 (batch_or_M = M), TRELLIS_OP_MOE_GEMV (L = any entry of the uniform
  * table: only in/out are read, batch_or_M ignored, n_routed = n).  Host pointer L.
  * Returns 0 for invalid arguments. */
 size_t trellis_workspace_bytes(int op, const trellis_linear *L, int batch_or_M, int n_routed);
@@ -123,6 +127,25 @@ int trellis_gemv(const trellis_linear *L, const uint16_t *x, int B, uint16_t *y,
  *     rotated activations). */
 int trellis_gemm(const trellis_linear *L, const uint16_t *x, int M, uint16_t *y,
                  void *ws, size_t ws_bytes, void *stream);
+
+/* Decode to E4M3 bytes (the cb = 2 weights): w8[16i + r][16j + c] = the E4M3 code of
+ * tile (i, j)'s element (r, c), i.e. the MCG codebook value rounded to E4M3.  Bit-exact.
+ * ("EXLR8" page, E4M3 paragraph: EXL3's decode followed by the E4M3 rounding.)
+ * code: int16 [in/16][out/16][16*K], 16-byte aligned; w8: uint8 out [in][out], 8-byte
+ * aligned.  in, out multiples of 16 (0 is a no-op). */
+int trellis_decode_tiles_e4m3(const int16_t *code, int K, int in_features, int out_features, uint8_t *w8,
+                              void *stream);
+
+/* Prefill on the FP8 matrix cores ("EXLR8" page: the E4M3 weights feed FP8 matrix
+ * multiplies).  L->cb must be 2.  With xh = had(x*su) per row:
+ *   sc_row = max|xh_row| / 448,  q = e4m3(xh_row / sc_row) (nearest even, saturating),
+ *   y = had(sc_row * (q @ W_hat)) * sv
+ * (an all-zero row gives y = 0).  x: fp16 [M][in], y: fp16 out [M][out], both 16-byte
+ * aligned.  ws: device workspace of >= trellis_workspace_bytes(
+ * TRELLIS_OP_GEMM_FP8, L, M, 0) bytes, 256-byte aligned (holds the E4M3 activations and
+ * row scales).  Three launches. */
+int trellis_gemm_fp8(const trellis_linear *L, const uint16_t *x, int M, uint16_t *y,
+                     void *ws, size_t ws_bytes, void *stream);
 
 /* Routed-expert products for one token: for k in [0, n), with e = routed[k],
  *   y[k] = had(had(x_k * su_e) @ W_hat_e) * sv_e,

@@ -160,3 +160,26 @@ def _mlp_call(L, **kw):
 def test_moe_mlp_validation(L, kw, status):
     assert _mlp_call(L, **kw) == status, L.trellis_last_error()
     assert L.trellis_last_error()
+
+
+def test_fp8_entry_validation(L):
+    c1, c2 = lin(), lin(cb=2)
+    need = L.trellis_workspace_bytes(3, ctypes.byref(c2), 64, 0)
+    assert need >= 64 * 512
+    assert L.trellis_gemm_fp8(ctypes.byref(c1), 0x60000, 64, 0x70000, 0x80000, need, None) == EINVAL  # cb=1
+    assert L.trellis_gemm_fp8(ctypes.byref(c2), 0x60000, -1, 0x70000, 0x80000, need, None) == EINVAL
+    assert L.trellis_gemm_fp8(ctypes.byref(c2), 0x60000, 0, 0x70000, 0x80000, need, None) == 0  # no-op
+    assert L.trellis_gemm_fp8(ctypes.byref(c2), 0x60008, 64, 0x70000, 0x80000, need, None) == EALIGN
+    assert L.trellis_gemm_fp8(ctypes.byref(c2), 0x60000, 64, 0x70000, 0x80000, need - 256, None) == EWORKSPACE
+    assert L.trellis_gemm_fp8(ctypes.byref(lin(cb=3)), 0x60000, 64, 0x70000, 0x80000, need, None) == EINVAL
+    # the fp16 products do not take the E4M3 codebook
+    assert L.trellis_gemv(ctypes.byref(c2), 0x60000, 1, 0x70000, 0x80000, 1 << 30, None) == -4
+    assert L.trellis_gemm(ctypes.byref(c2), 0x60000, 64, 0x70000, 0x80000, 1 << 30, None) == -4
+    # decode to E4M3 bytes
+    f = L.trellis_decode_tiles_e4m3
+    assert f(0x10000, 5, 64, 64, 0x20000, None) == EINVAL
+    assert f(0x10000, 2, 60, 64, 0x20000, None) == EINVAL
+    assert f(0x10000, 2, 0, 64, 0x20000, None) == 0
+    assert f(0x10008, 2, 64, 64, 0x20000, None) == EALIGN
+    assert f(0x10000, 2, 64, 64, 0x20004, None) == EALIGN
+    assert f(0x10000, 2, 64, 64, None, None) == EINVAL

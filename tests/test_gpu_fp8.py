@@ -1,0 +1,93 @@
+"""GPU parity of the FP8 variant (cb = 2, the E4M3 codebook) against the CPU oracle.
+
+trellis_decode_tiles_e4m3 must be bit-exact over every one of the 65 536 states.
+trellis_gemm_fp8 is compared with the oracle's FP8 prefill (the same per-row E4M3
+quantisation of the rotated activations, then fp64 arithmetic) within 2e-3 relative L2:
+E4M3 products are exact in the fp32 accumulator, so what remains is the accumulation order,
+the fp16 output and the rare activation code that the fp32 rotation puts on the other side
+of a rounding boundary than the fp64 one."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from trellis_coded_bit_amd import binding as tb
+from trellis_coded_bit_amd import synth
+
+from gpu_util import REL_L2_TOL, log_case, rel_l2, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+def test_decode_e4m3_bit_exact_all_states(K):
+    log_case(f"decode e4m3 K={K}")
+    lin = synth.make_linear(np.random.SeedSequence([50, K]), K, 1024, 2048)
+    st = O.tile_states(lin.code, K)
+    assert np.unique(st).size == 1 << 16  # every state occurs
+    w8 = tb.trellis_decode_tiles_e4m3(to_dev(lin.code), K)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(w8.cpu().numpy(), O.decode_tiles_e4m3(lin.code, K))
+
+
+def _fp8_linear(seed, K, n_in, n_out):
+    lin = synth.make_linear(np.random.SeedSequence(seed), K, n_in, n_out)
+    lin.cb = 2
+    return lin
+
+
+def _gemm_fp8_np(lin, x):
+    y = tb.trellis_gemm_fp8(tb.TrellisLinear.from_host(lin), to_dev(x))
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("M,n_in,n_out", [(1, 128, 128), (37, 384, 256), (600, 1024, 384), (513, 640, 128)])
+def test_gemm_fp8_small(K, M, n_in, n_out):
+    log_case(f"gemm fp8 K={K} M={M} {n_in}x{n_out}")
+    lin = _fp8_linear([51, K, M, n_in, n_out], K, n_in, n_out)
+    x = synth.make_x(np.random.SeedSequence([52, M]), M, n_in)
+    y = _gemm_fp8_np(lin, x)
+    ref = O.forward_linear(lin, x, act_e4m3=True)
+    assert rel_l2(y, ref) < REL_L2_TOL
+
+
+@pytest.mark.parametrize("wgs", ["3", "7", "50"])
+def test_gemm_fp8_split_tiles(monkeypatch, wgs):
+    """Few workgroups: tiles split between two and among several ranges."""
+    log_case(f"gemm fp8 wgs={wgs}")
+    monkeypatch.setenv("TRELLIS_GEMM_WGS", wgs)
+    lin = _fp8_linear([53, 3], 3, 1152, 384)
+    x = synth.make_x(np.random.SeedSequence(54), 700, 1152)
+    assert rel_l2(_gemm_fp8_np(lin, x), O.forward_linear(lin, x, act_e4m3=True)) < REL_L2_TOL
+
+
+def test_gemm_fp8_zero_rows_and_determinism():
+    lin = _fp8_linear([55, 2], 2, 256, 256)
+    x = synth.make_x(np.random.SeedSequence(56), 40, 256)
+    x[[0, 17, 39]] = 0
+    L = tb.TrellisLinear.from_host(lin)
+    xd = to_dev(x)
+    y1 = tb.trellis_gemm_fp8(L, xd).clone()
+    y2 = tb.trellis_gemm_fp8(L, xd)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    y = y1.cpu().numpy()
+    assert np.all(y[[0, 17, 39]] == 0)
+    assert rel_l2(y, O.forward_linear(lin, x, act_e4m3=True)) < REL_L2_TOL
+
+
+def test_gemm_fp8_prefill_full_size():
+    """K3 5120 -> 17408, M = 2048 (the prefill shape), sampled output column blocks."""
+    lin = _fp8_linear([57], 3, 5120, 17408)
+    x = synth.make_x(np.random.SeedSequence(58), 2048, 5120)
+    y = _gemm_fp8_np(lin, x)
+    blocks = [0, 77, 135]
+    ref = O.forward_linear(lin, x, col_blocks=blocks, act_e4m3=True)
+    got = np.concatenate([y[:, 128 * J:128 * J + 128] for J in blocks], axis=1)
+    assert rel_l2(got, ref) < REL_L2_TOL
+    # the FP8 path against the unquantised activations: the E4M3 rounding of xh costs a
+    # few percent, as the oracle's own band says
+    exact = O.forward_linear(lin, x[:64], col_blocks=blocks[:1])
+    assert 0.005 < rel_l2(y[:64, :128], exact) < 0.05

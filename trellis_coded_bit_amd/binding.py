@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtrellis.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "trellis.h")
 
-TRELLIS_OP_GEMV, TRELLIS_OP_GEMM, TRELLIS_OP_MOE_GEMV = 0, 1, 2
+TRELLIS_OP_GEMV, TRELLIS_OP_GEMM, TRELLIS_OP_MOE_GEMV, TRELLIS_OP_GEMM_FP8 = 0, 1, 2, 3
 TRELLIS_OP_MOE_MLP = 100  # workspace-cache key only (the C ABI has a dedicated size call)
 STATUS = {0: "TRELLIS_OK", -1: "TRELLIS_EINVAL", -2: "TRELLIS_EALIGN", -3: "TRELLIS_EWORKSPACE",
           -4: "TRELLIS_EUNSUPPORTED", -5: "TRELLIS_EHIP"}
@@ -78,6 +78,10 @@ def lib() -> ctypes.CDLL:
             L.trellis_gemm.argtypes = [ctypes.POINTER(CLinear), vp, i32, vp, vp, sz, vp]
             L.trellis_moe_gemv.restype = i32
             L.trellis_moe_gemv.argtypes = [vp, i32, vp, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, sz, vp]
+            L.trellis_decode_tiles_e4m3.restype = i32
+            L.trellis_decode_tiles_e4m3.argtypes = [vp, i32, i32, i32, vp, vp]
+            L.trellis_gemm_fp8.restype = i32
+            L.trellis_gemm_fp8.argtypes = [ctypes.POINTER(CLinear), vp, i32, vp, vp, sz, vp]
             L.trellis_moe_mlp_workspace_bytes.restype = sz
             L.trellis_moe_mlp_workspace_bytes.argtypes = [i32, i32, i32, i32]
             L.trellis_moe_mlp.restype = i32
@@ -144,8 +148,9 @@ class TrellisLinear:
     """Device tensors of one trellis-coded layer (y = x W, W [in, out])."""
 
     def __init__(self, code: torch.Tensor, rin: torch.Tensor, rout: torch.Tensor,
-                 s_in: Optional[torch.Tensor], s_out: Optional[torch.Tensor], K: int):
+                 s_in: Optional[torch.Tensor], s_out: Optional[torch.Tensor], K: int, cb: int = 1):
         self.code, self.rin, self.rout, self.s_in, self.s_out, self.K = code, rin, rout, s_in, s_out, int(K)
+        self.cb = int(cb)
         ti, tj, nw = code.shape
         self.in_features, self.out_features = 16 * ti, 16 * tj
         if nw != 16 * self.K:
@@ -165,12 +170,12 @@ class TrellisLinear:
     def from_host(cls, lin, device="cuda") -> "TrellisLinear":
         """From a ``synth.Linear`` (numpy arrays)."""
         t = lambda a: torch.from_numpy(a).to(device)
-        return cls(t(lin.code), t(lin.rin), t(lin.rout), t(lin.s_in), t(lin.s_out), lin.K)
+        return cls(t(lin.code), t(lin.rin), t(lin.rout), t(lin.s_in), t(lin.s_out), lin.K, getattr(lin, "cb", 1))
 
     def c(self) -> CLinear:
         if self._c is None:
             self._c = CLinear(_ptr(self.code), _ptr(self.rin), _ptr(self.rout), _ptr(self.s_in), _ptr(self.s_out),
-                              self.K, self.in_features, self.out_features, 1)
+                              self.K, self.in_features, self.out_features, self.cb)
         return self._c
 
     def workspace_bytes(self, op: int, batch_or_M: int) -> int:
@@ -253,6 +258,34 @@ def trellis_gemm(layer: TrellisLinear, x: torch.Tensor, out: Optional[torch.Tens
         raise ValueError(f"workspace of {ws.numel()} bytes < {nb}")
     _check(lib().trellis_gemm(ctypes.byref(layer.c()), x.data_ptr(), M, out.data_ptr(), ws.data_ptr(), ws.numel(),
                               _stream()))
+    return out
+
+
+def trellis_decode_tiles_e4m3(code: torch.Tensor, K: int) -> torch.Tensor:
+    """code int16 [in/16, out/16, 16K] -> E4M3 codes uint8 [in, out] (the cb = 2 weights)."""
+    _req(code, torch.int16, "code")
+    ti, tj, nw = code.shape
+    if nw != 16 * K:
+        raise ValueError("code last dim must be 16*K")
+    w8 = torch.empty((16 * ti, 16 * tj), dtype=torch.uint8, device=code.device)
+    _check(lib().trellis_decode_tiles_e4m3(code.data_ptr(), K, 16 * ti, 16 * tj, w8.data_ptr(), _stream()))
+    return w8
+
+
+def trellis_gemm_fp8(layer: TrellisLinear, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x fp16 [M, in] -> y fp16 [M, out] on the FP8 matrix cores (layer.cb must be 2)."""
+    _req(x, torch.float16, "x", layer.code.device)
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, layer.out_features), dtype=torch.float16, device=x.device)
+    nb = layer.workspace_bytes(TRELLIS_OP_GEMM_FP8, M)
+    if ws is None:
+        ws = workspace(nb, x.device, TRELLIS_OP_GEMM_FP8)
+    elif ws.numel() < nb:
+        raise ValueError(f"workspace of {ws.numel()} bytes < {nb}")
+    _check(lib().trellis_gemm_fp8(ctypes.byref(layer.c()), x.data_ptr(), M, out.data_ptr(), ws.data_ptr(),
+                                  ws.numel(), _stream()))
     return out
 
 

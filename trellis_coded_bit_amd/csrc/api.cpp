@@ -31,7 +31,8 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int check_linear(const trellis_linear *L, int need_side_vectors) {
   if (!L) return fail(TRELLIS_EINVAL, "layer descriptor is NULL");
   if (L->K < 2 || L->K > 4) return fail(TRELLIS_EINVAL, "K=%d not in {2,3,4}", L->K);
-  if (L->cb != 1) return fail(TRELLIS_EINVAL, "cb=%d: only the MCG codebook (cb=1) is defined", L->cb);
+  if (L->cb != 1 && L->cb != 2)
+    return fail(TRELLIS_EINVAL, "cb=%d: 1 (MCG codebook) or 2 (MCG rounded to E4M3) expected", L->cb);
   if (L->in_features <= 0 || L->out_features <= 0 || L->in_features % 128 || L->out_features % 128)
     return fail(TRELLIS_EINVAL, "in=%d out=%d must be positive multiples of 128", L->in_features,
                 L->out_features);
@@ -109,6 +110,9 @@ size_t trellis_workspace_bytes(int op, const trellis_linear *L, int batch_or_M, 
     case TRELLIS_OP_MOE_GEMV:
       if (n_routed < 0) return 0;
       return trellis::gemv_workspace_bytes(n_routed, L->in_features, L->out_features, 1);
+    case TRELLIS_OP_GEMM_FP8:
+      if (batch_or_M < 0) return 0;
+      return trellis::gemm_fp8_workspace_bytes(L->in_features, L->out_features, batch_or_M);
     default:
       return 0;
   }
@@ -119,6 +123,7 @@ int trellis_gemv(const trellis_linear *L, const uint16_t *x, int B, uint16_t *y,
   g_err[0] = 0;
   int st = check_linear(L, 1);
   if (st) return st;
+  if (L->cb != 1) return fail(TRELLIS_EUNSUPPORTED, "trellis_gemv: cb=%d is not supported", L->cb);
   if (B < 1 || B > 8) return fail(TRELLIS_EINVAL, "B=%d not in 1..8", B);
   if (!x || !y) return fail(TRELLIS_EINVAL, "x or y is NULL");
   if (!aligned(x, 2) || !aligned(y, 2)) return fail(TRELLIS_EALIGN, "x/y must be 2-byte aligned");
@@ -150,6 +155,7 @@ int trellis_gemm(const trellis_linear *L, const uint16_t *x, int M, uint16_t *y,
   g_err[0] = 0;
   int st = check_linear(L, 1);
   if (st) return st;
+  if (L->cb != 1) return fail(TRELLIS_EUNSUPPORTED, "trellis_gemm: cb=%d is not supported", L->cb);
   if (M < 0) return fail(TRELLIS_EINVAL, "M=%d < 0", M);
   if (M == 0) return TRELLIS_OK;
   if ((long long)M > (1LL << 24)) return fail(TRELLIS_EINVAL, "M=%d too large", M);
@@ -160,6 +166,38 @@ int trellis_gemm(const trellis_linear *L, const uint16_t *x, int M, uint16_t *y,
     return fail(TRELLIS_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
   return hip_status(trellis::launch_gemm(*L, x, M, y, ws, ws_bytes, as_stream(stream)),
                     "trellis_gemm launch");
+}
+
+int trellis_gemm_fp8(const trellis_linear *L, const uint16_t *x, int M, uint16_t *y, void *ws,
+                     size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  int st = check_linear(L, 1);
+  if (st) return st;
+  if (L->cb != 2) return fail(TRELLIS_EINVAL, "trellis_gemm_fp8 needs the E4M3 codebook (cb=2), got cb=%d", L->cb);
+  if (M < 0) return fail(TRELLIS_EINVAL, "M=%d < 0", M);
+  if (M == 0) return TRELLIS_OK;
+  if ((long long)M > (1LL << 24)) return fail(TRELLIS_EINVAL, "M=%d too large", M);
+  if (!x || !y) return fail(TRELLIS_EINVAL, "x or y is NULL");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(TRELLIS_EALIGN, "x/y must be 16-byte aligned");
+  const size_t need = trellis::gemm_fp8_workspace_bytes(L->in_features, L->out_features, M);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(TRELLIS_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+  return hip_status(trellis::launch_gemm_fp8(*L, x, M, y, ws, ws_bytes, as_stream(stream)),
+                    "trellis_gemm_fp8 launch");
+}
+
+int trellis_decode_tiles_e4m3(const int16_t *code, int K, int in_features, int out_features, uint8_t *w8,
+                              void *stream) {
+  g_err[0] = 0;
+  if (K < 2 || K > 4) return fail(TRELLIS_EINVAL, "K=%d not in {2,3,4}", K);
+  if (in_features < 0 || out_features < 0 || in_features % 16 || out_features % 16)
+    return fail(TRELLIS_EINVAL, "in=%d out=%d must be non-negative multiples of 16", in_features,
+                out_features);
+  if ((long long)in_features * out_features == 0) return TRELLIS_OK;
+  if (!code || !w8) return fail(TRELLIS_EINVAL, "code or w8 is NULL");
+  if (!aligned(code, 16) || !aligned(w8, 8)) return fail(TRELLIS_EALIGN, "code must be 16-byte and w8 8-byte aligned");
+  return hip_status(trellis::launch_decode_tiles_e4m3(code, K, in_features, out_features, w8, as_stream(stream)),
+                    "trellis_decode_tiles_e4m3 launch");
 }
 
 int trellis_moe_gemv(const trellis_linear *experts, int E, const int32_t *routed, int n,

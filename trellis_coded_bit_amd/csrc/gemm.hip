@@ -53,7 +53,9 @@ constexpr int kTileFloats = kMT * kNT;
 constexpr int kMinSteps = 4;  // fewest k-step pairs per workgroup worth a split
 
 struct GemmParams {
-  const uint16_t *xh;  // rotated activations in 16-row x k-step blocks (rotate_kernel)
+  const uint16_t *xh;  // rotated activations in 16-row x k-step blocks (rotate_kernel;
+                       // E4M3 bytes for the FP8 product)
+  const float *rowscale;  // FP8 product: per-row dequantisation scale [Mpad], else unused
   const uint32_t *code;
   const uint16_t *rout;
   const float *s_out;
@@ -224,12 +226,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
 }
 
 // Staging through LDS uses the wave's own 1 KB of B ring slot 0 (idle between pieces).
-__device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int mt, int nt, u32x4 (*ring)[8][64]) {
+// F8: the rows carry the activations' dequantisation scales (rowscale), applied with sv.
+template <bool F8 = false>
+__device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int mt, int nt, u32x4 *ring0) {
   const int lane = threadIdx.x & 63, n16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const float sg1 = (lane & 1) ? -1.f : 1.f, sg2 = (lane & 2) ? -1.f : 1.f;
   const float sg4 = (lane & 4) ? -1.f : 1.f, sg8 = (lane & 8) ? -1.f : 1.f;
-  uint16_t *stage = reinterpret_cast<uint16_t *>(&ring[0][wave][0]);
+  uint16_t *stage = reinterpret_cast<uint16_t *>(ring0 + (F8 ? 128 : 64) * wave);
   // the wave's 64 rows of the tile's output (uniform); stores to rows past M fall outside
   // the buffer range and are dropped
   const int wrow0 = mt * kMT + 64 * wave;
@@ -243,6 +247,17 @@ __device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int m
     if (P.s_out) s *= P.s_out[col];
     sv[nb] = s;
   }
+  uint32_t rs[4][4];  // f32 bits
+  if constexpr (F8) {
+    // rows past the padded row count read as zero (their stores are dropped anyway)
+    const int Mpad = (P.M + 15) & ~15;
+    const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(P.rowscale + wrow0, (long long)(Mpad - wrow0) * 4);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        rs[mb][r] = __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(16 * mb + 4 * (lane >> 4) + r) * 4, 0, 0);
+  }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
@@ -250,6 +265,10 @@ __device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int m
       float v[8];
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) v[nb] = acc[mb][nb][r];
+      if constexpr (F8) {
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) v[nb] *= __builtin_bit_cast(float, rs[mb][r]);
+      }
       // column strides 16, 32, 64: register index nb
 #pragma unroll
       for (int h = 1; h < 8; h <<= 1) {
@@ -467,10 +486,262 @@ __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][
   lds_barrier();  // the rings' last reads are done before the next piece writes them
 }
 
+// ---------------------------------------------------------------------------------------
+// The FP8 product ("EXLR8" page: decoded weights are exactly E4M3, so prefill runs on FP8
+// matrix multiplies).  The activations are rotated, then quantised per row to E4M3 with
+// the scale max|row| / 448 (two launches: the rows' block maxima, then the codes), and the
+// product runs on v_mfma_f32_16x16x128_f8f6f4 with k-steps of 128 input rows (eight
+// trellis tile rows).  A lane's 32 B operand: byte j is tile row j >> 2 of the step and the
+// lane's symbol j & 3 (rows 2g, 2g+1, 2g+8, 2g+9 of that tile, g = lane >> 4) -- for B the
+// four E4M3 bytes of one decoded tile are one register; A is stored in the same order.
+// ---------------------------------------------------------------------------------------
+
+// One 128-block of 16 rows rotated: thread (row q = tid >> 4, i = tid & 15) returns
+// elements 8i..8i+7 of H128(x*su) (unnormalised), zeros for rows past M.  VEC: r and s are
+// 16-byte aligned (vector loads), else element loads.
+template <bool VEC>
+__device__ __forceinline__ void rotate_block(const uint16_t *__restrict__ x, int rows, int n,
+                                             const uint16_t *__restrict__ r, const float *__restrict__ s, int row,
+                                             int c, float (&v)[8]) {
+  if (row < rows) {
+    const u32x4 xv = *reinterpret_cast<const u32x4 *>(x + (size_t)row * n + c);
+    float rv[8], sv[8];
+    if (VEC) {
+      const u32x4 r4 = *reinterpret_cast<const u32x4 *>(r + c);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) rv[t] = h2f((t & 1) ? (uint16_t)(r4[t >> 1] >> 16) : (uint16_t)r4[t >> 1]);
+      if (s) {
+        const floatx4 s0 = *reinterpret_cast<const floatx4 *>(s + c);
+        const floatx4 s1 = *reinterpret_cast<const floatx4 *>(s + c + 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          sv[t] = s0[t];
+          sv[t + 4] = s1[t];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        rv[t] = h2f(r[c + t]);
+        if (s) sv[t] = s[c + t];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t xw = xv[t >> 1];
+      const uint16_t xs = (t & 1) ? (uint16_t)(xw >> 16) : (uint16_t)xw;
+      v[t] = h2f(xs) * rv[t];
+      if (s) v[t] *= sv[t];
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = 0.f;
+  }
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if ((t & h) == 0) {
+        const float a = v[t], b = v[t + h];
+        v[t] = a + b;
+        v[t + h] = a - b;
+      }
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    float p;
+    p = lane_xor<1>(v[t]);
+    v[t] = (lane & 1) ? (p - v[t]) : (v[t] + p);
+    p = lane_xor<2>(v[t]);
+    v[t] = (lane & 2) ? (p - v[t]) : (v[t] + p);
+    p = lane_xor<4>(v[t]);
+    v[t] = (lane & 4) ? (p - v[t]) : (v[t] + p);
+    p = lane_xor<8>(v[t]);
+    v[t] = (lane & 8) ? (p - v[t]) : (v[t] + p);
+  }
+}
+
+// Maximum over the 16 lanes of a row (lanes 16q .. 16q+15 of a wave).
+__device__ __forceinline__ float row16_max(float m) {
+  m = fmaxf(m, lane_xor<1>(m));
+  m = fmaxf(m, lane_xor<2>(m));
+  m = fmaxf(m, lane_xor<4>(m));
+  m = fmaxf(m, lane_xor<8>(m));
+  return m;
+}
+
+// Launch 1: workgroup per (16-row block rb, 128-block blk); pmax[row][blk] = max |xh| of
+// the row over the block.  Also clears the split-tile counters.
+template <bool VEC>
+__global__ __launch_bounds__(256) void rowmax_kernel(const uint16_t *__restrict__ x, int rows, int n,
+                                                     const uint16_t *__restrict__ r, const float *__restrict__ s,
+                                                     float *__restrict__ pmax, uint32_t *__restrict__ counters,
+                                                     int ncounters) {
+  for (int c = blockIdx.x * 256 + threadIdx.x; c < ncounters; c += gridDim.x * 256) counters[c] = 0;
+  const int nb = n / 128;
+  const int rb = blockIdx.x / nb, blk = blockIdx.x - rb * nb;
+  const int q = threadIdx.x >> 4, i = threadIdx.x & 15;
+  const int row = 16 * rb + q;
+  float v[8];
+  rotate_block<VEC>(x, rows, n, r, s, row, blk * 128 + 8 * i, v);
+  float m = 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(v[t]));
+  m = row16_max(m);
+  if (i == 0) pmax[(size_t)row * nb + blk] = m;
+}
+
+// Launch 2: same grid.  The row's maximum a, the codes e4m3(xh * 448 / a) (clamped to
+// +-448 first, so the conversion never saturates), written as 2 KB blocks [row block]
+// [k-step] in the operand order above; block 0 also writes rowscale[row] = a / 448.
+template <bool VEC>
+__global__ __launch_bounds__(256) void quant8_kernel(const uint16_t *__restrict__ x, int rows, int n,
+                                                     const uint16_t *__restrict__ r, const float *__restrict__ s,
+                                                     const float *__restrict__ pmax, uint8_t *__restrict__ xq,
+                                                     float *__restrict__ rowscale) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[2048];
+  const int nb = n / 128;
+  const int rb = blockIdx.x / nb, blk = blockIdx.x - rb * nb;
+  const int q = threadIdx.x >> 4, i = threadIdx.x & 15;
+  const int row = 16 * rb + q;
+  float m = 0.f;
+  for (int b = i; b < nb; b += 16) m = fmaxf(m, pmax[(size_t)row * nb + b]);
+  m = row16_max(m);
+  const float inv = m > 0.f ? 448.0f / m : 0.f;
+  if (blk == 0 && i == 0) rowscale[row] = m * (1.0f / 448.0f);
+  float v[8];
+  rotate_block<VEC>(x, rows, n, r, s, row, blk * 128 + 8 * i, v);
+  // element 8i + t: tile row i >> 1 of the step, tile-internal row 8(i & 1) + t, so lane
+  // group g = t >> 1 and byte j = 4(i >> 1) + 2(i & 1) + (t & 1) of lane 16g + q
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const float a = fminf(fmaxf(v[2 * g] * inv, -448.f), 448.f);
+    const float b = fminf(fmaxf(v[2 * g + 1] * inv, -448.f), 448.f);
+    const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    *reinterpret_cast<uint16_t *>(stage + (16 * g + q) * 32 + 4 * (i >> 1) + 2 * (i & 1)) = (uint16_t)pk;
+  }
+  __syncthreads();
+  uint8_t *out = xq + ((size_t)rb * nb + blk) * 2048;
+  reinterpret_cast<uint2 *>(out)[threadIdx.x] = reinterpret_cast<const uint2 *>(stage)[threadIdx.x];
+}
+
+typedef int intx8 __attribute__((ext_vector_type(8)));
+
+// Accumulates k-steps [k0, k1) of tile t (128 input rows each) on the FP8 matrix core.
+// B ring: [2 slots][8 column blocks][2 halves][64 lanes] (2 KB per column block); code
+// ring: per wave [4 slots][64 chunks of 16 B] (the step's eight tiles of the wave's column
+// block, tile ti at chunks 2K*ti ..).
 template <int K>
-__global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  // 2 waves per SIMD
-  __shared__ __attribute__((aligned(16))) u32x4 ring[2][8][64];         // decoded B operands
-  __shared__ __attribute__((aligned(16))) u32x4 cring[kWaves][4 * 2 * 32 / 4];  // staged codes
+__device__ __forceinline__ void run_piece_f8(const GemmParams &P, u32x4 (*ring)[8][2][64], u32x4 (*cring)[4 * 64],
+                                             int t, int k0, int k1, Acc &acc, int signal) {
+  constexpr int NW = 8 * K;  // 32-bit words per trellis tile
+  constexpr int CH = 2 * K;  // 16-byte chunks per trellis tile
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int mt = t / P.nNT, nt = t - mt * P.nNT;
+  const LaneWindow lw = lane_window(lane, K);
+  // A: 2 KB blocks [row block][step]; the lane's 32 bytes at 32 * lane.  Blocks past the
+  // last row block read as zero.
+  const int row0 = mt * kMT + 64 * wave;
+  const int Mpad = (P.M + 15) & ~15;
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(reinterpret_cast<const uint8_t *>(P.xh) + (size_t)(row0 >> 4) * P.S * 2048,
+                                                (long long)(Mpad - row0) * P.in);
+  const uint32_t a_off = (uint32_t)lane * 32;
+  const int a_mb = P.S * 2048;  // bytes between row blocks
+  // Codes: column block `wave`, tile rows 8s .. 8s+7; lane loads chunk lane % (8 CH).
+  const long long row_bytes = (long long)(P.out / 16) * NW * 4;
+  const long long code_bytes = (long long)(P.in / 16) * row_bytes;
+  const long long col_off = (long long)(nt * 8 + wave) * NW * 4;
+  const int cc = lane % (8 * CH);
+  const uint32_t c_off = (uint32_t)((cc / CH) * row_bytes + 16 * (cc % CH));
+  u32x4 *cw = cring[wave];
+
+  auto load_a = [&](u32x4 (&a)[4][2], int st) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) a[mb][h] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_off, st * 2048 + mb * a_mb + 16 * h, 0);
+  };
+  auto load_c = [&](u32x4 &c, int st) {
+    const long long off = 8LL * st * row_bytes + col_off;
+    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(reinterpret_cast<const char *>(P.code) + off, code_bytes - off);
+    c = __builtin_amdgcn_raw_buffer_load_b128(rc, c_off, 0, 0);
+  };
+  auto stage_c = [&](const u32x4 &c, int slot) { cw[slot * 64 + cc] = c; };  // repeated lanes store equal data
+  auto decode_to = [&](int cslot, int slot) {
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(cw + cslot * 64);
+    uint32_t q[8];
+#pragma unroll
+    for (int ti = 0; ti < 8; ++ti) {
+      const uint32_t bits = lane_bits(w[ti * NW + lw.d0], w[ti * NW + lw.d1], lw.sh);
+      q[ti] = e4m3_pack4(mcg_hash(lane_state<K>(bits, 0)), mcg_hash(lane_state<K>(bits, 1)),
+                         mcg_hash(lane_state<K>(bits, 2)), mcg_hash(lane_state<K>(bits, 3)));
+    }
+    ring[slot][wave][0][lane] = u32x4{q[0], q[1], q[2], q[3]};
+    ring[slot][wave][1][lane] = u32x4{q[4], q[5], q[6], q[7]};
+  };
+  auto mfma_step = [&](const u32x4 (&a)[4][2], int slot) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const u32x4 b0 = ring[slot][nb][0][lane], b1 = ring[slot][nb][1][lane];
+      const intx8 bv = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const intx8 av = {(int)a[mb][0][0], (int)a[mb][0][1], (int)a[mb][0][2], (int)a[mb][0][3],
+                          (int)a[mb][1][0], (int)a[mb][1][1], (int)a[mb][1][2], (int)a[mb][1][3]};
+        acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mb][nb], 0, 0, 0, 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 A0[4][2], A1[4][2];
+  u32x4 CR0, CR1;
+  // Step s (relative r = s - k0) uses B ring slot r & 1 and A registers of that parity; its
+  // codes sit in code ring slot r & 3.  During step s the codes of step s+1 are decoded
+  // into the other B slot and those of step s+2 staged; codes and activations are loaded
+  // two steps ahead (past the piece they fetch unused data, bounded by the resources).
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the previous piece's stores are done
+  load_c(CR0, k0);
+  load_a(A0, k0);
+  load_c(CR1, k0 + 1);
+  load_a(A1, k0 + 1);
+  stage_c(CR0, 0);
+  load_c(CR0, k0 + 2);
+  stage_c(CR1, 1);
+  load_c(CR1, k0 + 3);
+  decode_to(0, 0);
+  lds_barrier();
+  if (signal >= 0 && threadIdx.x == 0)
+    __hip_atomic_fetch_add(P.counters + 2 * signal + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int st = k0, r = 0; st < k1; st += 2, r += 2) {
+    // step st: B slot 0, A0
+    stage_c(CR0, (r + 2) & 3);
+    load_c(CR0, st + 4);
+    decode_to((r + 1) & 3, 1);  // step st + 1
+    mfma_step(A0, 0);
+    lds_barrier();
+    load_a(A0, st + 2);
+    if (st + 1 < k1) {  // (uniform) step st + 1: B slot 1, A1
+      stage_c(CR1, (r + 3) & 3);
+      load_c(CR1, st + 5);
+      decode_to((r + 2) & 3, 0);  // step st + 2
+      mfma_step(A1, 1);
+      lds_barrier();
+      load_a(A1, st + 3);
+    }
+  }
+  lds_barrier();  // the rings' last reads are done before the next piece writes them
+}
+
+// The workgroup's range: pieces, split tiles, epilogues (shared by the fp16 and FP8 products).
+template <int K, bool F8, typename Ring, typename CRing>
+__device__ __forceinline__ void gemm_ranges(const GemmParams &P, Ring ring, CRing cring) {
   __shared__ uint32_t arrivals;
   const int g = xcd_range(blockIdx.x, P.G);
   const int it0 = range_start(P, g);
@@ -489,7 +760,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
     const int k0 = t == tf ? it0 - ts : 0;
     const int k1 = t == tl ? end - ts : P.S;
     Acc acc;
-    run_piece<K>(P, ring, cring, t, k0, k1, acc, signal);
+    if constexpr (F8) run_piece_f8<K>(P, ring, cring, t, k0, k1, acc, signal);
+    else run_piece<K>(P, ring, cring, t, k0, k1, acc, signal);
     signal = -1;
     bool finish = k0 == 0 && k1 == P.S;  // one epilogue call site (register allocation)
     if (!finish) {
@@ -537,13 +809,27 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  /
         }
       }
     }
-    if (finish) finish_tile(P, acc, t / P.nNT, t % P.nNT, ring);
+    if (finish) finish_tile<F8>(P, acc, t / P.nNT, t % P.nNT, reinterpret_cast<u32x4 *>(ring));
   }
   if (signal >= 0) {
     __syncthreads();  // the stores of the last piece's partial have completed
     if (threadIdx.x == 0)
       __hip_atomic_fetch_add(P.counters + 2 * signal + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+template <int K>
+__global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  // 2 waves per SIMD
+  __shared__ __attribute__((aligned(16))) u32x4 ring[2][8][64];         // decoded B operands
+  __shared__ __attribute__((aligned(16))) u32x4 cring[kWaves][4 * 2 * 32 / 4];  // staged codes
+  gemm_ranges<K, false>(P, ring, cring);
+}
+
+template <int K>
+__global__ __launch_bounds__(kThreads, 2) void gemm_f8_kernel(GemmParams P) {  // 2 waves per SIMD
+  __shared__ __attribute__((aligned(16))) u32x4 ring[2][8][2][64];  // decoded B operands (E4M3)
+  __shared__ __attribute__((aligned(16))) u32x4 cring[kWaves][4 * 64];  // staged codes
+  gemm_ranges<K, true>(P, ring, cring);
 }
 
 int device_cu_count() {
@@ -562,12 +848,14 @@ struct Plan {
   int S, nNT, T, G;
   long long I;
   int q, r;
-  size_t xh_bytes, partials_off, counters_off, bytes;
+  size_t xh_bytes, pmax_off, rowscale_off, partials_off, counters_off, bytes;
 };
 
-Plan plan(int in_features, int out_features, int M) {
+// f8: iterations are single 128-row k-steps and the activations are E4M3 bytes, with the
+// row maxima and scales after them.
+Plan plan(int in_features, int out_features, int M, bool f8 = false) {
   Plan p;
-  p.S = in_features / (2 * kKS);
+  p.S = f8 ? in_features / 128 : in_features / (2 * kKS);
   p.nNT = out_features / kNT;
   p.T = (M + kMT - 1) / kMT * p.nNT;
   p.I = (long long)p.T * p.S;
@@ -584,8 +872,11 @@ Plan plan(int in_features, int out_features, int M) {
   p.G = (int)G;
   p.q = (int)(p.I / G);
   p.r = (int)(p.I % G);
-  p.xh_bytes = (size_t)((M + 15) / 16) * 16 * in_features * 2;  // whole 16-row blocks
-  p.partials_off = p.xh_bytes;
+  const size_t Mpad = (size_t)((M + 15) / 16) * 16;  // whole 16-row blocks
+  p.xh_bytes = Mpad * in_features * (f8 ? 1 : 2);
+  p.pmax_off = p.xh_bytes;
+  p.rowscale_off = p.pmax_off + (f8 ? (Mpad * (in_features / 128) * 4 + 255) / 256 * 256 : 0);
+  p.partials_off = p.rowscale_off + (f8 ? (Mpad * 4 + 255) / 256 * 256 : 0);
   p.counters_off = p.partials_off + (size_t)2 * p.G * kTileFloats * sizeof(float);
   p.bytes = p.counters_off + ((size_t)p.T * 8 + 255) / 256 * 256;
   return p;
@@ -596,6 +887,60 @@ Plan plan(int in_features, int out_features, int M) {
 size_t gemm_workspace_bytes(int in_features, int out_features, int M) {
   if (M <= 0) return 256;
   return plan(in_features, out_features, M).bytes;
+}
+
+size_t gemm_fp8_workspace_bytes(int in_features, int out_features, int M) {
+  if (M <= 0) return 256;
+  return plan(in_features, out_features, M, true).bytes;
+}
+
+hipError_t launch_gemm_fp8(const trellis_linear &L, const uint16_t *x, int M, uint16_t *y, void *ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const Plan p = plan(L.in_features, L.out_features, M, true);
+  if (ws_bytes < p.bytes) return hipErrorInvalidValue;
+  if (p.G > (1 << 20)) return hipErrorInvalidValue;
+  if (p.I >= (1LL << 31)) return hipErrorInvalidValue;  // 32-bit iteration arithmetic
+  if ((long long)(M + 15) / 16 * (L.in_features / 128) >= (1LL << 31)) return hipErrorInvalidValue;
+  char *w = static_cast<char *>(ws);
+  uint8_t *xq = reinterpret_cast<uint8_t *>(w);
+  float *pmax = reinterpret_cast<float *>(w + p.pmax_off);
+  float *rowscale = reinterpret_cast<float *>(w + p.rowscale_off);
+  uint32_t *counters = reinterpret_cast<uint32_t *>(w + p.counters_off);
+  const unsigned rgrid = (unsigned)((M + 15) / 16 * (L.in_features / 128));
+  const bool vec = (reinterpret_cast<uintptr_t>(L.rin) % 16) == 0 && (reinterpret_cast<uintptr_t>(L.s_in) % 16) == 0;
+  if (vec) rowmax_kernel<true><<<rgrid, 256, 0, stream>>>(x, M, L.in_features, L.rin, L.s_in, pmax, counters, 2 * p.T);
+  else rowmax_kernel<false><<<rgrid, 256, 0, stream>>>(x, M, L.in_features, L.rin, L.s_in, pmax, counters, 2 * p.T);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (vec) quant8_kernel<true><<<rgrid, 256, 0, stream>>>(x, M, L.in_features, L.rin, L.s_in, pmax, xq, rowscale);
+  else quant8_kernel<false><<<rgrid, 256, 0, stream>>>(x, M, L.in_features, L.rin, L.s_in, pmax, xq, rowscale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  GemmParams P;
+  P.xh = reinterpret_cast<const uint16_t *>(xq);
+  P.rowscale = rowscale;
+  P.code = reinterpret_cast<const uint32_t *>(L.code);
+  P.rout = L.rout;
+  P.s_out = L.s_out;
+  P.y = y;
+  P.partials = reinterpret_cast<float *>(w + p.partials_off);
+  P.counters = counters;
+  P.M = M;
+  P.in = L.in_features;
+  P.out = L.out_features;
+  P.S = p.S;
+  P.nNT = p.nNT;
+  P.G = p.G;
+  P.q = p.q;
+  P.r = p.r;
+  switch (L.K) {
+    case 2: gemm_f8_kernel<2><<<p.G, kThreads, 0, stream>>>(P); break;
+    case 3: gemm_f8_kernel<3><<<p.G, kThreads, 0, stream>>>(P); break;
+    case 4: gemm_f8_kernel<4><<<p.G, kThreads, 0, stream>>>(P); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const trellis_linear &L, const uint16_t *x, int M, uint16_t *y, void *ws,
@@ -618,6 +963,7 @@ hipError_t launch_gemm(const trellis_linear &L, const uint16_t *x, int M, uint16
   if (e != hipSuccess) return e;
   GemmParams P;
   P.xh = xh;
+  P.rowscale = nullptr;
   P.code = reinterpret_cast<const uint32_t *>(L.code);
   P.rout = L.rout;
   P.s_out = L.s_out;

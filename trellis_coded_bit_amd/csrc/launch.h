@@ -12,6 +12,9 @@ namespace trellis {
 hipError_t launch_decode_tiles(const int16_t *code, int K, int in_features, int out_features,
                                uint16_t *w_hat, uint16_t *states, hipStream_t stream);
 
+hipError_t launch_decode_tiles_e4m3(const int16_t *code, int K, int in_features, int out_features, uint8_t *w8,
+                                    hipStream_t stream);
+
 // y = had(x*r*s)*norm (post = 0) or had(x)*r*s*norm (post = 1) on 128-blocks; had() is
 // the UNNORMALISED Sylvester butterfly, `norm` the factor applied (1/sqrt(128) for the
 // public entry point).
@@ -74,5 +77,10 @@ hipError_t launch_moe_mlp(const MlpLaunch &m, void *ws, size_t ws_bytes, hipStre
 size_t gemm_workspace_bytes(int in_features, int out_features, int M);
 hipError_t launch_gemm(const trellis_linear &L, const uint16_t *x, int M, uint16_t *y, void *ws,
                        size_t ws_bytes, hipStream_t stream);
+
+// The FP8 prefill: E4M3 weights (cb = 2) against E4M3 activations with per-row scales.
+size_t gemm_fp8_workspace_bytes(int in_features, int out_features, int M);
+hipError_t launch_gemm_fp8(const trellis_linear &L, const uint16_t *x, int M, uint16_t *y, void *ws,
+                           size_t ws_bytes, hipStream_t stream);
 
 }  // namespace trellis

@@ -39,6 +39,30 @@ __device__ __forceinline__ _Float16 mcg_value(uint32_t h) {
   return lo + hi;
 }
 
+// Codebook values of two hash words as an fp16 pair (a in the low half, b in the high
+// half): the lo and hi halves are gathered into two registers and added as packed fp16, one
+// round-to-nearest-even per value.
+__device__ __forceinline__ uint32_t mcg_value2(uint32_t a, uint32_t b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x05040100u);  // (a.lo, b.lo)
+  const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07060302u);  // (a.hi, b.hi)
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, lo) + __builtin_bit_cast(h2, hi));
+}
+
+// The E4M3 codebook ("EXLR8" page, E4M3 paragraph: every codebook value is rounded to E4M3,
+// nearest with ties to even, saturating).  Four hash words -> their fp16 values -> four
+// E4M3 bytes, value j in byte j.  gfx950's scaled conversion with scale 1.0 rounds to
+// nearest even; the codebook's magnitudes stay below 4, far inside E4M3's range of 448, so
+// how it saturates never matters here.
+__device__ __forceinline__ uint32_t e4m3_pack4(uint32_t h0, uint32_t h1, uint32_t h2, uint32_t h3) {
+  typedef _Float16 hv2 __attribute__((ext_vector_type(2)));
+  typedef short sv2 __attribute__((ext_vector_type(2)));
+  const sv2 zero = {0, 0};
+  sv2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(zero, __builtin_bit_cast(hv2, mcg_value2(h0, h1)), 1.0f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, __builtin_bit_cast(hv2, mcg_value2(h2, h3)), 1.0f, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // Per-lane window geometry inside a tile of K-bit symbols (8K 32-bit words).
 // The lane's four windows start at stream bit `start` = K*s0 + K - 16 (mod 256K).
 // Writing start = 32*d0 + off with off in [1, 32], the 32 stream bits beginning at `start`
