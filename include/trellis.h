@@ -63,8 +63,8 @@ typedef enum {
  * nearest, ties to even, saturating), the EXLR8 format's codebook.
  * ("The escha W2 format, recovered and verified", "Tensor mapping": the config tensor
  *  [16, bits, cb, 1, in, out] fixes tile 16, K = bits, cb; "EXLR8" page, E4M3 paragraph.)
- * trellis_gemv, trellis_gemm and the MoE calls take cb = 1 (cb = 2: TRELLIS_EUNSUPPORTED,
- * or a zero row for a table entry); trellis_gemm_fp8 takes cb = 2. */
+ * Every product takes either codebook per matrix (table entries may mix them);
+ * trellis_gemm_fp8 requires cb = 2. */
 typedef struct {
   const int16_t *code;
   const uint16_t *rin;

@@ -379,11 +379,11 @@ def moe_forward(layer, routed: Iterable[int], x_token: np.ndarray, x_down: np.nd
     for k, e in enumerate(routed):
         ge, ue, de = layer.gate[e], layer.up[e], layer.down[e]
         g.append(forward(ge.code, ge.K, layer.r_hidden_in, ge.rout, layer.s_hidden_in, ge.s_out,
-                         x_token, cb_gu)[0])
+                         x_token, cb_gu, cb=getattr(ge, "cb", 1))[0])
         u.append(forward(ue.code, ue.K, layer.r_hidden_in, ue.rout, layer.s_hidden_in, ue.s_out,
-                         x_token, cb_gu)[0])
+                         x_token, cb_gu, cb=getattr(ue, "cb", 1))[0])
         d.append(forward(de.code, de.K, de.rin, layer.r_hidden_out, de.s_in, layer.s_hidden_out,
-                         x_down[k:k + 1], cb_d)[0])
+                         x_down[k:k + 1], cb_d, cb=getattr(de, "cb", 1))[0])
     return np.stack(g), np.stack(u), np.stack(d)
 
 
@@ -417,14 +417,15 @@ def moe_mlp_forward(layer, routed: Sequence[int], router_w: Sequence[float], x_t
     x = np.atleast_2d(np.asarray(x_token))
     acts, y = [], np.zeros(layer.hidden)
     for k, e in enumerate(routed):
-        g = np.concatenate([forward(l.code, l.K, layer.r_hidden_in, l.rout, layer.s_hidden_in, l.s_out, x)[0]
-                            for l in layer.gate[e]])
-        u = np.concatenate([forward(l.code, l.K, layer.r_hidden_in, l.rout, layer.s_hidden_in, l.s_out, x)[0]
-                            for l in layer.up[e]])
+        cbk = lambda l: getattr(l, "cb", 1)  # each matrix's own codebook
+        g = np.concatenate([forward(l.code, l.K, layer.r_hidden_in, l.rout, layer.s_hidden_in, l.s_out, x,
+                                    cb=cbk(l))[0] for l in layer.gate[e]])
+        u = np.concatenate([forward(l.code, l.K, layer.r_hidden_in, l.rout, layer.s_hidden_in, l.s_out, x,
+                                    cb=cbk(l))[0] for l in layer.up[e]])
         a = silu(g) * u
         d = layer.down[e]
         y = y + float(router_w[k]) * forward(d.code, d.K, d.rin, layer.r_hidden_out, d.s_in,
-                                             layer.s_hidden_out, a[None, :])[0]
+                                             layer.s_hidden_out, a[None, :], cb=cbk(d))[0]
         acts.append(a)
     act = np.stack(acts) if acts else np.zeros((0, layer.inter))
     return (y, act) if return_act else y

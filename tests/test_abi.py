@@ -172,9 +172,10 @@ def test_fp8_entry_validation(L):
     assert L.trellis_gemm_fp8(ctypes.byref(c2), 0x60008, 64, 0x70000, 0x80000, need, None) == EALIGN
     assert L.trellis_gemm_fp8(ctypes.byref(c2), 0x60000, 64, 0x70000, 0x80000, need - 256, None) == EWORKSPACE
     assert L.trellis_gemm_fp8(ctypes.byref(lin(cb=3)), 0x60000, 64, 0x70000, 0x80000, need, None) == EINVAL
-    # the fp16 products do not take the E4M3 codebook
-    assert L.trellis_gemv(ctypes.byref(c2), 0x60000, 1, 0x70000, 0x80000, 1 << 30, None) == -4
-    assert L.trellis_gemm(ctypes.byref(c2), 0x60000, 64, 0x70000, 0x80000, 1 << 30, None) == -4
+    # an unknown codebook is rejected by every product
+    c3 = lin(cb=3)
+    assert L.trellis_gemv(ctypes.byref(c3), 0x60000, 1, 0x70000, 0x80000, 1 << 30, None) == EINVAL
+    assert L.trellis_gemm(ctypes.byref(c3), 0x60000, 64, 0x70000, 0x80000, 1 << 30, None) == EINVAL
     # decode to E4M3 bytes
     f = L.trellis_decode_tiles_e4m3
     assert f(0x10000, 5, 64, 64, 0x20000, None) == EINVAL

@@ -91,3 +91,76 @@ def test_gemm_fp8_prefill_full_size():
     # few percent, as the oracle's own band says
     exact = O.forward_linear(lin, x[:64], col_blocks=blocks[:1])
     assert 0.005 < rel_l2(y[:64, :128], exact) < 0.05
+
+
+# ------------------------------------------------------------------------------------------
+# The E4M3 codebook in the fp16-activation products (GEMV, MoE, MLP, prefill)
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("n_in,n_out,B", [(384, 640, 1), (1152, 256, 3), (640, 384, 8)])
+def test_gemv_e4m3_codebook(K, n_in, n_out, B):
+    log_case(f"gemv e4m3 K={K} {n_in}x{n_out} B={B}")
+    lin = _fp8_linear([60, K, n_in, n_out, B], K, n_in, n_out)
+    x = synth.make_x(np.random.SeedSequence([61, B]), B, n_in)
+    y = tb.trellis_gemv(tb.TrellisLinear.from_host(lin), to_dev(x))
+    torch.cuda.synchronize()
+    assert rel_l2(y.cpu().numpy(), O.forward_linear(lin, x)) < REL_L2_TOL
+
+
+def test_gemv_e4m3_codebook_full_size():
+    """up_proj shape K3 5120 -> 17408 with the E4M3 codebook, batch 1, sampled blocks."""
+    lin = _fp8_linear([62], 3, 5120, 17408)
+    x = synth.make_x(np.random.SeedSequence(63), 1, 5120)
+    y = tb.trellis_gemv(tb.TrellisLinear.from_host(lin), to_dev(x))
+    torch.cuda.synchronize()
+    blocks = [0, 70, 135]
+    ref = O.forward_linear(lin, x, col_blocks=blocks)
+    got = np.concatenate([y.cpu().numpy()[:, 128 * J:128 * J + 128] for J in blocks], axis=1)
+    assert rel_l2(got, ref) < REL_L2_TOL
+
+
+def test_moe_table_mixing_codebooks():
+    lins = []
+    for e, (K, cb) in enumerate([(2, 1), (3, 2), (4, 2), (2, 2), (3, 1), (4, 1)]):
+        l = synth.make_linear(np.random.SeedSequence([64, e]), K, 256, 384)
+        l.cb = cb
+        lins.append(l)
+    table = tb.ExpertTable([tb.TrellisLinear.from_host(l) for l in lins])
+    routed = np.array([1, 0, 5, 2, 3, 2], np.int32)
+    x = synth.make_x(np.random.SeedSequence(65), 1, 256)
+    y = tb.trellis_moe_gemv(table, to_dev(routed), to_dev(x[0]), False)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    for k, e in enumerate(routed):
+        assert rel_l2(y[k], O.forward_linear(lins[e], x)[0]) < REL_L2_TOL, (k, e)
+    assert tb.moe_error_word() == 0
+
+
+def test_mlp_with_e4m3_slices():
+    """A routed MLP whose gate/up slices and down matrices mix the two codebooks."""
+    layer = synth.moe_mlp_layer(7, n_experts=4, hidden=256, inter=256, halves=2)
+    for e in range(4):
+        layer.gate[e][e % 2].cb = 2
+        layer.up[e][1 - e % 2].cb = 2
+        if e % 2:
+            layer.down[e].cb = 2
+    tables = tb.MoEMLPTables.from_host(layer)
+    routed, w = [3, 0, 1], [0.5, 0.25, 0.25]
+    x = synth.make_x(np.random.SeedSequence(66), 1, 256)
+    y = tb.trellis_moe_mlp(tables, to_dev(np.array(routed, np.int32)), to_dev(np.array(w, np.float32)),
+                           to_dev(x[0]), tables.r_hidden_in, tables.s_hidden_in, tables.r_hidden_out,
+                           tables.s_hidden_out)
+    torch.cuda.synchronize()
+    assert rel_l2(y.cpu().numpy(), O.moe_mlp_forward(layer, routed, w, x)) < REL_L2_TOL
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+def test_gemm_fp16_e4m3_codebook(K):
+    """trellis_gemm (fp16 activations) on E4M3 weights: the cb = 2 forward, no activation
+    quantisation."""
+    lin = _fp8_linear([67, K], K, 640, 384)
+    x = synth.make_x(np.random.SeedSequence(68), 300, 640)
+    y = tb.trellis_gemm(tb.TrellisLinear.from_host(lin), to_dev(x))
+    torch.cuda.synchronize()
+    assert rel_l2(y.cpu().numpy(), O.forward_linear(lin, x)) < REL_L2_TOL

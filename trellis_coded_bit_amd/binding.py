@@ -373,7 +373,8 @@ class MoEMLPTables:
         t = lambda a: torch.from_numpy(a).to(device)
         r_hi, s_hi = t(layer.r_hidden_in), t(layer.s_hidden_in)
         r_ho, s_ho = t(layer.r_hidden_out), t(layer.s_hidden_out)
-        dev = lambda l, rin, s_in, rout, s_out: TrellisLinear(t(l.code), rin, rout, s_in, s_out, l.K)
+        dev = lambda l, rin, s_in, rout, s_out: TrellisLinear(t(l.code), rin, rout, s_in, s_out, l.K,
+                                                              getattr(l, "cb", 1))
         E = len(layer.down)
         gate = [[dev(l, r_hi, s_hi, t(l.rout), t(l.s_out)) for l in layer.gate[e]] for e in range(E)]
         up = [[dev(l, r_hi, s_hi, t(l.rout), t(l.s_out)) for l in layer.up[e]] for e in range(E)]

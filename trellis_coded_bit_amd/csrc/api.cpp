@@ -123,7 +123,6 @@ int trellis_gemv(const trellis_linear *L, const uint16_t *x, int B, uint16_t *y,
   g_err[0] = 0;
   int st = check_linear(L, 1);
   if (st) return st;
-  if (L->cb != 1) return fail(TRELLIS_EUNSUPPORTED, "trellis_gemv: cb=%d is not supported", L->cb);
   if (B < 1 || B > 8) return fail(TRELLIS_EINVAL, "B=%d not in 1..8", B);
   if (!x || !y) return fail(TRELLIS_EINVAL, "x or y is NULL");
   if (!aligned(x, 2) || !aligned(y, 2)) return fail(TRELLIS_EALIGN, "x/y must be 2-byte aligned");
@@ -155,7 +154,6 @@ int trellis_gemm(const trellis_linear *L, const uint16_t *x, int M, uint16_t *y,
   g_err[0] = 0;
   int st = check_linear(L, 1);
   if (st) return st;
-  if (L->cb != 1) return fail(TRELLIS_EUNSUPPORTED, "trellis_gemm: cb=%d is not supported", L->cb);
   if (M < 0) return fail(TRELLIS_EINVAL, "M=%d < 0", M);
   if (M == 0) return TRELLIS_OK;
   if ((long long)M > (1LL << 24)) return fail(TRELLIS_EINVAL, "M=%d too large", M);

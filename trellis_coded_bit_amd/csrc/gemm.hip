@@ -184,8 +184,9 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t *__restrict_
 }
 
 // Four symbols of one tile for this lane -> fp16 codebook values packed in pairs
-// (symbols 0,1 and 2,3: tile rows 2g, 2g+1 and 2g+8, 2g+9 of column n).
-template <int K>
+// (symbols 0,1 and 2,3: tile rows 2g, 2g+1 and 2g+8, 2g+9 of column n).  CB = 2: each
+// value rounded to E4M3 and converted back to fp16 (exact), the E4M3 codebook ("EXLR8").
+template <int K, int CB = 1>
 __device__ __forceinline__ u32x2 decode_pairs(uint32_t w0, uint32_t w1, uint32_t sh) {
   const uint32_t bits = lane_bits(w0, w1, sh);
   uint32_t h[4];
@@ -198,6 +199,11 @@ __device__ __forceinline__ u32x2 decode_pairs(uint32_t w0, uint32_t w1, uint32_t
     const uint32_t hi = __builtin_amdgcn_perm(h[2 * p + 1], h[2 * p], 0x07060302u);  // hi halves
     const half2_t v = __builtin_bit_cast(half2_t, lo) + __builtin_bit_cast(half2_t, hi);
     out[p] = __builtin_bit_cast(uint32_t, v);
+    if constexpr (CB == 2) {
+      typedef short sv2 __attribute__((ext_vector_type(2)));
+      const sv2 q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(sv2{0, 0}, v, 1.0f, false);
+      out[p] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_bit_cast(uint32_t, q), 1.0f, false));
+    }
   }
   return out;
 }
@@ -342,7 +348,7 @@ __device__ __forceinline__ void add_partial(const GemmParams &P, int slot, Acc &
 }
 
 // Accumulates k-step pairs [k0, k1) of tile t (k-steps 2*k0 .. 2*k1 - 1).
-template <int K>
+template <int K, int CB = 1>
 __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][64],
                                           u32x4 (*cring)[4 * 2 * 32 / 4], int t, int k0, int k1, Acc &acc,
                                           int signal) {
@@ -393,8 +399,8 @@ __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][
   };
   auto decode_to = [&](int cslot, int slot) {
     const uint32_t *w = cw + cslot * 2 * NW;
-    const u32x2 t0 = decode_pairs<K>(w[lw.d0], w[lw.d1], lw.sh);
-    const u32x2 t1 = decode_pairs<K>(w[NW + lw.d0], w[NW + lw.d1], lw.sh);
+    const u32x2 t0 = decode_pairs<K, CB>(w[lw.d0], w[lw.d1], lw.sh);
+    const u32x2 t1 = decode_pairs<K, CB>(w[NW + lw.d0], w[NW + lw.d1], lw.sh);
     ring[slot][wave][lane] = u32x4{t0[0], t0[1], t1[0], t1[1]};
   };
   // B operands of one step: column blocks 0..3 are read from the ring right after the
@@ -740,7 +746,8 @@ __device__ __forceinline__ void run_piece_f8(const GemmParams &P, u32x4 (*ring)[
 }
 
 // The workgroup's range: pieces, split tiles, epilogues (shared by the fp16 and FP8 products).
-template <int K, bool F8, typename Ring, typename CRing>
+// F8: the FP8 product; CB: the codebook of the fp16 product.
+template <int K, bool F8, int CB, typename Ring, typename CRing>
 __device__ __forceinline__ void gemm_ranges(const GemmParams &P, Ring ring, CRing cring) {
   __shared__ uint32_t arrivals;
   const int g = xcd_range(blockIdx.x, P.G);
@@ -761,7 +768,7 @@ __device__ __forceinline__ void gemm_ranges(const GemmParams &P, Ring ring, CRin
     const int k1 = t == tl ? end - ts : P.S;
     Acc acc;
     if constexpr (F8) run_piece_f8<K>(P, ring, cring, t, k0, k1, acc, signal);
-    else run_piece<K>(P, ring, cring, t, k0, k1, acc, signal);
+    else run_piece<K, CB>(P, ring, cring, t, k0, k1, acc, signal);
     signal = -1;
     bool finish = k0 == 0 && k1 == P.S;  // one epilogue call site (register allocation)
     if (!finish) {
@@ -818,18 +825,18 @@ __device__ __forceinline__ void gemm_ranges(const GemmParams &P, Ring ring, CRin
   }
 }
 
-template <int K>
+template <int K, int CB>
 __global__ __launch_bounds__(kThreads, 2) void gemm_sk_kernel(GemmParams P) {  // 2 waves per SIMD
   __shared__ __attribute__((aligned(16))) u32x4 ring[2][8][64];         // decoded B operands
   __shared__ __attribute__((aligned(16))) u32x4 cring[kWaves][4 * 2 * 32 / 4];  // staged codes
-  gemm_ranges<K, false>(P, ring, cring);
+  gemm_ranges<K, false, CB>(P, ring, cring);
 }
 
 template <int K>
 __global__ __launch_bounds__(kThreads, 2) void gemm_f8_kernel(GemmParams P) {  // 2 waves per SIMD
   __shared__ __attribute__((aligned(16))) u32x4 ring[2][8][2][64];  // decoded B operands (E4M3)
   __shared__ __attribute__((aligned(16))) u32x4 cring[kWaves][4 * 64];  // staged codes
-  gemm_ranges<K, true>(P, ring, cring);
+  gemm_ranges<K, true, 1>(P, ring, cring);
 }
 
 int device_cu_count() {
@@ -978,10 +985,13 @@ hipError_t launch_gemm(const trellis_linear &L, const uint16_t *x, int M, uint16
   P.G = p.G;
   P.q = p.q;
   P.r = p.r;
-  switch (L.K) {
-    case 2: gemm_sk_kernel<2><<<p.G, kThreads, 0, stream>>>(P); break;
-    case 3: gemm_sk_kernel<3><<<p.G, kThreads, 0, stream>>>(P); break;
-    case 4: gemm_sk_kernel<4><<<p.G, kThreads, 0, stream>>>(P); break;
+  switch (L.K + 4 * (L.cb - 1)) {
+    case 2: gemm_sk_kernel<2, 1><<<p.G, kThreads, 0, stream>>>(P); break;
+    case 3: gemm_sk_kernel<3, 1><<<p.G, kThreads, 0, stream>>>(P); break;
+    case 4: gemm_sk_kernel<4, 1><<<p.G, kThreads, 0, stream>>>(P); break;
+    case 6: gemm_sk_kernel<2, 2><<<p.G, kThreads, 0, stream>>>(P); break;
+    case 7: gemm_sk_kernel<3, 2><<<p.G, kThreads, 0, stream>>>(P); break;
+    case 8: gemm_sk_kernel<4, 2><<<p.G, kThreads, 0, stream>>>(P); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

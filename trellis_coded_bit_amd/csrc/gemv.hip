@@ -89,6 +89,7 @@ struct Problem {
   const uint16_t *rin, *rout;
   const float *s_in, *s_out;
   int K;
+  int cb;  // 1: MCG fp16 values; 2: the same rounded to E4M3
   bool ok;
 };
 
@@ -107,6 +108,7 @@ __device__ __forceinline__ Problem get_problem(const GemvParams &P, int p) {
   Problem r;
   r.code = reinterpret_cast<const uint32_t *>(d.code);
   r.K = d.K;
+  r.cb = d.cb;
   r.rin = d.rin;
   r.s_in = d.s_in;
   r.rout = d.rout;
@@ -114,7 +116,7 @@ __device__ __forceinline__ Problem get_problem(const GemvParams &P, int p) {
   if (P.L.shared_side == 0) { r.rin = P.L.shared_r; r.s_in = P.L.shared_s; }
   if (P.L.shared_side == 1) { r.rout = P.L.shared_r; r.s_out = P.L.shared_s; }
   if (ok) {
-    ok = d.K >= 2 && d.K <= 4 && d.cb == 1 && d.code != nullptr && r.rin != nullptr &&
+    ok = d.K >= 2 && d.K <= 4 && (d.cb == 1 || d.cb == 2) && d.code != nullptr && r.rin != nullptr &&
          r.rout != nullptr && d.in_features == P.L.in_features &&
          d.out_features == P.L.out_features;
   }
@@ -282,7 +284,10 @@ __device__ __forceinline__ void dma_unit(const uint32_t *row0, size_t row_stride
 // Units [ub, ue) of problem p (width K), in sub-ranges of at most P.kA units.  Each
 // sub-range issues its rotation loads and its first code copies, rotates while the code is
 // in flight, then streams with SLOTS - 1 units in flight per wave.
-template <int K>
+// CB = 2 (the E4M3 codebook, "EXLR8" page): each lane's four values are the E4M3-rounded
+// codebook values, converted back to fp16 (exact) and fed to v_mfma_f32_16x16x16_f16 with
+// the A operand's duplicated words repacked once per tile row into (x0, x1), (x8, x9).
+template <int K, int CB = 1>
 __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &pr, int p, int ub, int ue,
                             bool fresh) {
   using RG = Ring<K>;
@@ -399,6 +404,7 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
       for (int r = 0; r < 2; ++r) {
         const u32x4 a = *reinterpret_cast<const u32x4 *>(sm.a + (uint32_t)(((k * 8 + 2 * wave + r) * 4 * B) << 2) + a_lane);
         const half8 av = __builtin_bit_cast(half8, a);
+        const u32x2 a2 = {__builtin_amdgcn_perm(a[1], a[0], 0x05040100u), __builtin_amdgcn_perm(a[3], a[2], 0x05040100u)};
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
           const uint32_t *tw = ub_ + (r * 8 + tt) * NW;
@@ -408,7 +414,15 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
           bw[1] = mcg_hash(lane_state<K>(bits, 1));
           bw[2] = mcg_hash(lane_state<K>(bits, 2));
           bw[3] = mcg_hash(lane_state<K>(bits, 3));
-          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8, bw), acc[tt], 0, 0, 0);
+          if constexpr (CB == 1) {
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8, bw), acc[tt], 0, 0, 0);
+          } else {
+            const uint32_t q = e4m3_pack4(bw[0], bw[1], bw[2], bw[3]);
+            const half2_t v01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q, 1.0f, false);
+            const half2_t v23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q, 1.0f, true);
+            const half4_t bv = {v01[0], v01[1], v23[0], v23[1]};
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a2), bv, acc[tt], 0, 0, 0);
+          }
         }
       }
       wave_sync();
@@ -435,7 +449,7 @@ __device__ void run_invalid(const GemvParams &P, const Lds &sm, int ub, int ue) 
 
 // KS = 2, 3, 4: one layer of that width (no table, the K dispatch compiled away, a smaller
 // kernel); KS = 0: a list of problems with per-entry K.
-template <int KS>
+template <int KS, int CBS = 1>
 __global__ __launch_bounds__(kThreads, 4) void gemv_partial_kernel(GemvParams P) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   const Lds sm = lds_carve(lds_raw, P.L.B, P.kA);
@@ -451,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_partial_kernel(GemvParams P)
   const int g = blockIdx.x;
   const int u0 = wg_start(g, P.U, P.G), u1 = wg_start(g + 1, P.U, P.G);
   if constexpr (KS != 0) {
-    if (u0 < u1) run_problem<KS>(P, sm, get_problem<false>(P, 0), 0, u0, u1, true);
+    if (u0 < u1) run_problem<KS, CBS>(P, sm, get_problem<false>(P, 0), 0, u0, u1, true);
     return;
   }
   const int per_problem = P.nI * P.nJ;
@@ -460,10 +474,13 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_partial_kernel(GemvParams P)
     const int ue = min(u1, (p + 1) * per_problem);
     const Problem pr = get_problem(P, p);
     const bool fresh = u == u0;
-    switch (pr.ok ? pr.K : 0) {
+    switch (pr.ok ? pr.K + 4 * (pr.cb - 1) : 0) {
       case 2: run_problem<2>(P, sm, pr, p, u, ue, fresh); break;
       case 3: run_problem<3>(P, sm, pr, p, u, ue, fresh); break;
       case 4: run_problem<4>(P, sm, pr, p, u, ue, fresh); break;
+      case 6: run_problem<2, 2>(P, sm, pr, p, u, ue, fresh); break;
+      case 7: run_problem<3, 2>(P, sm, pr, p, u, ue, fresh); break;
+      case 8: run_problem<4, 2>(P, sm, pr, p, u, ue, fresh); break;
       default: run_invalid(P, sm, u, ue); break;
     }
     u = ue;
@@ -740,9 +757,13 @@ hipError_t launch_gemv_parts(const GemvLaunch &a, uint32_t *errword, float *part
   P.maxseg = gm.maxseg;
   P.kA = gm.kA;
   const size_t lds = lds_bytes(a.B, gm.kA);
-  if (a.table == nullptr && a.single.K == 2) gemv_partial_kernel<2><<<gm.G, kThreads, lds, stream>>>(P);
-  else if (a.table == nullptr && a.single.K == 3) gemv_partial_kernel<3><<<gm.G, kThreads, lds, stream>>>(P);
-  else if (a.table == nullptr && a.single.K == 4) gemv_partial_kernel<4><<<gm.G, kThreads, lds, stream>>>(P);
+  const int single = a.table == nullptr ? a.single.K + 4 * (a.single.cb - 1) : 0;
+  if (single == 2) gemv_partial_kernel<2><<<gm.G, kThreads, lds, stream>>>(P);
+  else if (single == 3) gemv_partial_kernel<3><<<gm.G, kThreads, lds, stream>>>(P);
+  else if (single == 4) gemv_partial_kernel<4><<<gm.G, kThreads, lds, stream>>>(P);
+  else if (single == 6) gemv_partial_kernel<2, 2><<<gm.G, kThreads, lds, stream>>>(P);
+  else if (single == 7) gemv_partial_kernel<3, 2><<<gm.G, kThreads, lds, stream>>>(P);
+  else if (single == 8) gemv_partial_kernel<4, 2><<<gm.G, kThreads, lds, stream>>>(P);
   else gemv_partial_kernel<0><<<gm.G, kThreads, lds, stream>>>(P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -24,6 +24,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
 // The MCG hash ("Codebook: cb=1"): v = s * 0xCBAC1FED mod 2^32, then (v & 0x8FFF8FFF) ^
 // 0x3B603B60.  The result, read as two fp16 halves, sums to the codebook value.
