@@ -13,7 +13,7 @@ Sources (cited by page title and section; no line numbers):
   rotation paragraph, the calibration paragraph (the expert MLP's activation), the
   width-manifest paragraph (per-half widths) and the E4M3 paragraph (the FP8 codebook).
 
-Readings taken where the pages are silent or disagree are named A1..A25 in the
+Readings taken where the pages are silent or disagree are named A1..A26 in the
 docstrings and listed in the design notes.  Every function here follows the plain
 definition; nothing is blocked, fused or reordered beyond what the definition states.
 """
@@ -441,7 +441,8 @@ def symbol_order(tiles: np.ndarray) -> np.ndarray:
     return np.asarray(tiles)[:, r, c]
 
 
-def viterbi_encode(targets: np.ndarray, K: int, batch: int = 16) -> np.ndarray:
+def viterbi_encode(targets: np.ndarray, K: int, batch: int = 16, cb: int = 1,
+                   dtype=np.float64) -> np.ndarray:
     """Minimum squared-error tail-biting trellis paths: [T, 16, 16] -> states uint16 [T, 256].
 
     [EXLR8] tile-coding paragraph: a tile is a path through a 16-bit-state trellis, each
@@ -452,9 +453,18 @@ def viterbi_encode(targets: np.ndarray, K: int, batch: int = 16) -> np.ndarray:
     best end state; its low 16-K bits O fix the wrap.  Pass 2 restricts the start to
     states whose high 16-K bits are O and the end to states whose low 16-K bits are O,
     which makes the path close on itself.  Ties go to the lowest index (argmin).
+
+    cb = 2: the per-step values are the E4M3 codebook's ([EXLR8] E4M3 paragraph: the
+    rounding happens inside the search).  ``dtype``: the arithmetic of the path costs.  Each
+    step computes cost = best + (x - value)^2 as a subtraction, a multiplication and an
+    addition, each rounded once in that type; with float32 the minima and argmins are the
+    decisions a float32 search takes (reading A26).
     """
-    x_all = symbol_order(targets).astype(np.float64)
-    cb = codebook_table().astype(np.float64)
+    x_all = symbol_order(targets).astype(dtype)
+    table = codebook_table().astype(np.float64)
+    if cb == 2:
+        table = e4m3_round(table)
+    cb = table.astype(dtype)
     lowbits = 16 - K
     mask_lo = (1 << lowbits) - 1
     n_all = np.arange(1 << 16)
@@ -462,18 +472,20 @@ def viterbi_encode(targets: np.ndarray, K: int, batch: int = 16) -> np.ndarray:
 
     def run(x, start_ok, end_ok):
         T = x.shape[0]
-        cost = (x[:, 0, None] - cb[None, :]) ** 2
+        d = x[:, 0, None] - cb[None, :]
+        cost = d * d
         if start_ok is not None:
-            cost = np.where(start_ok, cost, np.inf)
+            cost = np.where(start_ok, cost, dtype(np.inf))
         back = np.empty((256, T, 1 << lowbits), np.uint8)
         for s in range(1, 256):
             c3 = cost.reshape(T, 1 << K, 1 << lowbits)  # [T, top K bits t, middle m]
             t_best = np.argmin(c3, axis=1)  # predecessor p = (t << lowbits) | m
             best = np.take_along_axis(c3, t_best[:, None, :], axis=1)[:, 0, :]
             back[s] = t_best
-            cost = np.repeat(best, 1 << K, axis=1) + (x[:, s, None] - cb[None, :]) ** 2
+            d = x[:, s, None] - cb[None, :]
+            cost = np.repeat(best, 1 << K, axis=1) + d * d
         if end_ok is not None:
-            cost = np.where(end_ok, cost, np.inf)
+            cost = np.where(end_ok, cost, dtype(np.inf))
         end = np.argmin(cost, axis=1)
         states = np.empty((T, 256), np.int64)
         states[:, 255] = end

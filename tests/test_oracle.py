@@ -289,6 +289,33 @@ def test_viterbi_pack_decode_round_trip(K):
         np.testing.assert_array_equal(dec[16 * t + r, c], O.codebook(path[t]))
 
 
+@pytest.mark.parametrize("K", [2, 4])
+def test_viterbi_e4m3_codebook_and_float32_search(K):
+    """cb = 2: the path's decoded values (E4M3 decode) are the E4M3 codebook values at the
+    path, and no path scores better under that codebook than the search's (checked against
+    the cb = 1 path re-scored with E4M3 values).  float32 search: a valid tail-biting path
+    whose float64 cost is within 1e-5 of the float64 search's."""
+    rng = np.random.default_rng(40 + K)
+    tgt = (rng.standard_normal((5, 16, 16)) * O.CODEBOOK_SCALE).astype(np.float32)
+    x = O.symbol_order(tgt).astype(np.float64)
+    v16 = O.codebook_table().astype(np.float64)
+    v8 = O.e4m3_round(v16)
+    p8 = O.viterbi_encode(tgt, K, cb=2, dtype=np.float32)
+    words = O.pack_states(p8, K)
+    np.testing.assert_array_equal(O.tile_states(words, K), p8)
+    dec = O.decode_tiles(words.reshape(5, 1, 16 * K), K, cb=2).astype(np.float64)
+    r, c = O.symbol_position(np.arange(256))
+    for t in range(5):
+        np.testing.assert_array_equal(dec[16 * t + r, c], v8[p8[t]])
+    p16 = O.viterbi_encode(tgt, K)
+    cost8 = ((x - v8[p8]) ** 2).sum(1)
+    assert np.all(cost8 <= ((x - v8[p16]) ** 2).sum(1) * (1 + 1e-6))
+    p32 = O.viterbi_encode(tgt, K, dtype=np.float32)
+    np.testing.assert_array_equal(O.tile_states(O.pack_states(p32, K), K), p32)
+    c32, c64 = ((x - v16[p32]) ** 2).sum(1), ((x - v16[p16]) ** 2).sum(1)
+    np.testing.assert_allclose(c32, c64, rtol=1e-5)
+
+
 def _shannon_relf(K, n_tiles=32, planted_offset=False):
     """[METAL] Shannon-bound paragraph, [EXLR8] rotation paragraphs: rotate a heavy-tailed
     matrix with random signs and the Hadamard on both sides, scale it to the codebook's
