@@ -204,6 +204,29 @@ int trellis_moe_mlp(const trellis_linear *gate_up, const trellis_linear *down, i
                     const uint16_t *r_hidden_out, const float *s_hidden_out, uint16_t *act,
                     uint16_t *y, void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of workspace trellis_encode_tiles needs for n_tiles tiles (1 MiB per tile: the
+ * search's decisions), 0 for n_tiles < 0. */
+size_t trellis_encode_workspace_bytes(int n_tiles);
+
+/* Tail-biting Viterbi encoder (the encode side of the format): for each 16x16 tile of
+ * target values, the path through the 16-bit-state trellis (each symbol adds K bits) whose
+ * codebook values have the least squared error, packed as the decoder reads it.
+ * ("EXLR8" page, tile-coding paragraph; its E4M3 paragraph for cb = 2, where the search
+ *  scores the E4M3-rounded values.)  The circular constraint: a first pass with a free
+ * start gives the best end state n1; its low 16-K bits O fix the wrap; the second pass
+ * starts from states with high bits O and ends in states with low bits O, so the path
+ * closes.  Ties go to the lowest state index.  Path costs are float32: each step adds
+ * (x - value)^2 computed as one subtraction, one multiplication and one addition, each
+ * rounded (no fused multiply-add).
+ * targets: f32 [n_tiles][16][16] (row = input row r, column = output column c of the
+ *          tile, in the codebook domain: rotated and scaled as the decoder's W_hat);
+ * code   : int16 out [n_tiles][16K] (tile words; trellis_decode_tiles reads them back);
+ * states : optional uint16 out [n_tiles][256], the path's states in symbol order;
+ * ws     : device workspace of >= trellis_encode_workspace_bytes(n_tiles), 256-byte aligned.
+ * Two launches: the search (one 1024-thread workgroup per tile) and the backtrack. */
+int trellis_encode_tiles(const float *targets, int n_tiles, int K, int cb, int16_t *code, uint16_t *states,
+                         void *ws, size_t ws_bytes, void *stream);
+
 /* Host-side check of a HOST copy of an expert table: K, cb, sizes, alignment, non-NULL
  * pointers (rin/rout may be NULL on a side that will be shared).  Returns TRELLIS_OK or the
  * first failing status (with the entry index in trellis_last_error()). */

@@ -184,3 +184,18 @@ def test_fp8_entry_validation(L):
     assert f(0x10008, 2, 64, 64, 0x20000, None) == EALIGN
     assert f(0x10000, 2, 64, 64, 0x20004, None) == EALIGN
     assert f(0x10000, 2, 64, 64, None, None) == EINVAL
+
+
+def test_encode_validation(L):
+    f = L.trellis_encode_tiles
+    need = L.trellis_encode_workspace_bytes(4)
+    assert need >= 4 * (1 << 20) and L.trellis_encode_workspace_bytes(-1) == 0
+    ok = dict(t=0x10000, T=4, K=2, cb=1, code=0x20000, st=None, ws=0x100000, nb=need)
+    call = lambda **kw: f(*[{**ok, **kw}[k] for k in ("t", "T", "K", "cb", "code", "st", "ws", "nb")], None)
+    assert call(K=5) == EINVAL and call(K=1) == EINVAL
+    assert call(cb=0) == EINVAL and call(cb=3) == EINVAL
+    assert call(T=-1) == EINVAL
+    assert call(T=0) == 0
+    assert call(t=None) == EINVAL and call(code=None) == EINVAL
+    assert call(t=0x10002) == EALIGN and call(code=0x20002) == EALIGN and call(st=0x30001) == EALIGN
+    assert call(nb=need - 1) == EWORKSPACE and call(ws=None) == EWORKSPACE and call(ws=0x100010) == EWORKSPACE

@@ -82,6 +82,10 @@ def lib() -> ctypes.CDLL:
             L.trellis_decode_tiles_e4m3.argtypes = [vp, i32, i32, i32, vp, vp]
             L.trellis_gemm_fp8.restype = i32
             L.trellis_gemm_fp8.argtypes = [ctypes.POINTER(CLinear), vp, i32, vp, vp, sz, vp]
+            L.trellis_encode_workspace_bytes.restype = sz
+            L.trellis_encode_workspace_bytes.argtypes = [i32]
+            L.trellis_encode_tiles.restype = i32
+            L.trellis_encode_tiles.argtypes = [vp, i32, i32, i32, vp, vp, vp, sz, vp]
             L.trellis_moe_mlp_workspace_bytes.restype = sz
             L.trellis_moe_mlp_workspace_bytes.argtypes = [i32, i32, i32, i32]
             L.trellis_moe_mlp.restype = i32
@@ -287,6 +291,25 @@ def trellis_gemm_fp8(layer: TrellisLinear, x: torch.Tensor, out: Optional[torch.
     _check(lib().trellis_gemm_fp8(ctypes.byref(layer.c()), x.data_ptr(), M, out.data_ptr(), ws.data_ptr(),
                                   ws.numel(), _stream()))
     return out
+
+
+def trellis_encode_tiles(targets: torch.Tensor, K: int, cb: int = 1, want_states: bool = False,
+                         ws: Optional[torch.Tensor] = None):
+    """targets f32 [T, 16, 16] -> (code int16 [T, 16K], states uint16-as-int16 [T, 256] or None)."""
+    _req(targets, torch.float32, "targets")
+    if targets.dim() != 3 or tuple(targets.shape[1:]) != (16, 16):
+        raise ValueError("targets must be [T, 16, 16]")
+    T = targets.shape[0]
+    code = torch.empty((T, 16 * K), dtype=torch.int16, device=targets.device)
+    st = torch.empty((T, 256), dtype=torch.int16, device=targets.device) if want_states else None
+    nb = lib().trellis_encode_workspace_bytes(T)
+    if ws is None:
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=targets.device)
+    elif ws.numel() < nb:
+        raise ValueError(f"workspace of {ws.numel()} bytes < {nb}")
+    _check(lib().trellis_encode_tiles(targets.data_ptr(), T, K, cb, code.data_ptr(), _ptr(st), ws.data_ptr(),
+                                      ws.numel(), _stream()))
+    return code, st
 
 
 class ExpertTable:

@@ -288,6 +288,29 @@ int trellis_moe_mlp(const trellis_linear *gate_up, const trellis_linear *down, i
   return hip_status(trellis::launch_moe_mlp(m, ws, ws_bytes, as_stream(stream)), "trellis_moe_mlp launch");
 }
 
+size_t trellis_encode_workspace_bytes(int n_tiles) {
+  if (n_tiles < 0) return 0;
+  return trellis::encode_workspace_bytes(n_tiles);
+}
+
+int trellis_encode_tiles(const float *targets, int n_tiles, int K, int cb, int16_t *code, uint16_t *states,
+                         void *ws, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  if (K < 2 || K > 4) return fail(TRELLIS_EINVAL, "K=%d not in {2,3,4}", K);
+  if (cb != 1 && cb != 2) return fail(TRELLIS_EINVAL, "cb=%d: 1 (MCG) or 2 (E4M3) expected", cb);
+  if (n_tiles < 0) return fail(TRELLIS_EINVAL, "n_tiles=%d < 0", n_tiles);
+  if (n_tiles == 0) return TRELLIS_OK;
+  if (!targets || !code) return fail(TRELLIS_EINVAL, "targets or code is NULL");
+  if (!aligned(targets, 4) || !aligned(code, 4) || !aligned(states, 2))
+    return fail(TRELLIS_EALIGN, "targets/code must be 4-byte and states 2-byte aligned");
+  const size_t need = trellis::encode_workspace_bytes(n_tiles);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(TRELLIS_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+  return hip_status(trellis::launch_encode_tiles(targets, n_tiles, K, cb, code, states, ws, ws_bytes,
+                                                 as_stream(stream)),
+                    "trellis_encode_tiles launch");
+}
+
 int trellis_validate_table(const trellis_linear *host_table, int E, int in_features,
                            int out_features, int shared_side) {
   g_err[0] = 0;

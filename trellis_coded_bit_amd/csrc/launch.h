@@ -72,6 +72,11 @@ struct MlpLaunch {
   uint16_t *y;
 };
 size_t moe_mlp_workspace_bytes(int hidden, int inter, int halves, int n);
+
+// Tail-biting Viterbi encoder: targets f32 [T][16][16] -> code [T][16K] (+ states).
+size_t encode_workspace_bytes(int n_tiles);
+hipError_t launch_encode_tiles(const float *targets, int T, int K, int cb, int16_t *code, uint16_t *states,
+                               void *ws, size_t ws_bytes, hipStream_t stream);
 hipError_t launch_moe_mlp(const MlpLaunch &m, void *ws, size_t ws_bytes, hipStream_t stream);
 
 size_t gemm_workspace_bytes(int in_features, int out_features, int M);
