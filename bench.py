@@ -449,13 +449,47 @@ def run_moe_mlp(args, torch, tb, synth):
             "unfused_ms_per_token": round(res["unfused"], 5) if "unfused" in res else None, "tokens_timed": steps}
 
 
+def run_encode(args, torch, tb, synth):
+    """trellis_encode_tiles on 2048 tiles of N(0, 1.24^2) targets (2 GiB of decisions),
+    K = 2, 3, 4, MCG codebook; the oracle's float32 search timed beside it on a few tiles."""
+    import oracle as O
+    T = 2048
+    rng = np.random.default_rng(args.seed)
+    tgt_h = (rng.standard_normal((T, 16, 16)) * 1.24371088).astype(np.float32)
+    tgt = torch.from_numpy(tgt_h).cuda()
+    ws = torch.empty(tb.lib().trellis_encode_workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    out = {"workload": f"tail-biting Viterbi encode (trellis_encode_tiles), {T} tiles of 16x16 N(0, 1.24^2) targets, "
+                       "MCG codebook", "per_K": {}}
+    for K in (2, 3, 4):
+        for _ in range(2):
+            tb.trellis_encode_tiles(tgt, K, ws=ws)
+        torch.cuda.synchronize()
+        n = 3
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(n):
+            tb.trellis_encode_tiles(tgt, K, ws=ws)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / n
+        t0 = time.perf_counter()
+        nt = 2
+        O.viterbi_encode(tgt_h[:nt], K, dtype=np.float32)
+        cpu_s = (time.perf_counter() - t0) / nt
+        out["per_K"][K] = {"ms_per_call": round(ms, 3), "tiles_per_s": round(T / (ms * 1e-3), 1),
+                           "weights_per_s": round(256 * T / (ms * 1e-3), 1),
+                           "state_steps_per_s": round(2 * 256 * 65536 * T / (ms * 1e-3), 1),
+                           "cpu_oracle_tiles_per_s": round(1.0 / cpu_s, 3)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--workload", default="dense", choices=["dense", "small_batch", "moe", "moe_mlp", "prefill"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "small_batch", "moe", "moe_mlp", "prefill", "encode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-unfused", action="store_true", help="moe_mlp: time only the fused call")
@@ -490,6 +524,8 @@ def main():
         print(json.dumps(run_moe(args, torch, tb, synth)), flush=True)
     elif args.workload == "moe_mlp":
         print(json.dumps(run_moe_mlp(args, torch, tb, synth)), flush=True)
+    elif args.workload == "encode":
+        print(json.dumps(run_encode(args, torch, tb, synth)), flush=True)
     else:
         print(json.dumps(run_prefill(args, torch, tb, synth)), flush=True)
         print(json.dumps(run_prefill(args, torch, tb, synth, fp8=True)), flush=True)
