@@ -71,12 +71,35 @@ def cpu_baseline_dense(wl, budget_s: float = 12.0):
         blocks += 1
         k += 1
     dt = time.perf_counter() - t0
+    # the two parts separately, on one block of up_proj: decode (codes -> W_hat) and the
+    # fp64 forward with W_hat given
+    lin = wl.layers["up"]
+    sub = np.ascontiguousarray(lin.code[:, 0:8, :])
+    t_dec = 1e9
+    for _ in range(3):  # (best of three: the first call also warms numpy up)
+        t1 = time.perf_counter()
+        w = O.decode_tiles(sub, lin.K).astype(np.float64)
+        t_dec = min(t_dec, time.perf_counter() - t1)
+    xh = O.had_blocks(wl.xs["up"].astype(np.float64) * O.side_scale(lin.rin, lin.s_in))
+    t2 = time.perf_counter()
+    for _ in range(20):
+        O.had_blocks(xh @ w)
+    t_fwd = (time.perf_counter() - t2) / 20
+    blk_bytes = lin.in_features * 128 * lin.K // 8
+    cpu_model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"{blocks} whole 128-column output blocks (decode + fp64 forward) of the gate/up/down "
                       f"matrices, round robin, {nbytes / 1e6:.1f} MB of code in {dt:.1f} s; host "
-                      f"{platform.processor() or platform.machine()}, os.cpu_count()={os.cpu_count()}, "
+                      f"{cpu_model}, os.cpu_count()={os.cpu_count()}, "
                       f"affinity={len(os.sched_getaffinity(0))}, numpy decode single-threaded, "
-                      f"BLAS threads={blas_threads}"}
+                      f"BLAS threads={blas_threads}",
+            "decode_only_GBps": round(blk_bytes / t_dec / 1e9, 6),
+            "forward_only_GBps_of_code": round(blk_bytes / t_fwd / 1e9, 4)}
 
 
 def gemv_source_sha256() -> str:
