@@ -150,9 +150,10 @@ def test_moe_small(shared_side, x_per_expert):
     routed = np.array([5, 0, 3, 3, 1, 4, 2], np.int32)
     n = len(routed)
     x = synth.make_x(np.random.SeedSequence(13), n if x_per_expert else 1, 256)
+    ws = torch.zeros(table.workspace_bytes(len(routed)), dtype=torch.uint8, device="cuda")  # own error word
     y = tb.trellis_moe_gemv(table, to_dev(routed), to_dev(x if x_per_expert else x[0]), x_per_expert,
                             to_dev(sr) if shared_side >= 0 else None, to_dev(ss) if shared_side >= 0 else None,
-                            shared_side)
+                            shared_side, ws=ws)
     torch.cuda.synchronize()
     y = y.cpu().numpy().astype(np.float64)
     for k, e in enumerate(routed):
@@ -165,7 +166,7 @@ def test_moe_small(shared_side, x_per_expert):
         xe = x[k:k + 1] if x_per_expert else x[0:1]
         ref = O.forward(l.code, l.K, rin, rout, s_in, s_out, xe)[0]
         assert rel_l2(y[k], ref) < REL_L2_TOL, (k, e)
-    assert tb.moe_error_word() == 0
+    assert int(ws[:4].view(torch.int32).item()) == 0
 
 
 def test_moe_bad_entries_give_zero_rows_and_error_word():
@@ -179,12 +180,13 @@ def test_moe_bad_entries_give_zero_rows_and_error_word():
     table.table = torch.frombuffer(raw, dtype=torch.uint8).cuda()
     routed = to_dev(np.array([0, 1, 7, 2], np.int32))  # entry 1 bad K, id 7 out of range
     x = to_dev(synth.make_x(np.random.SeedSequence(3), 1, 256)[0])
-    y = tb.trellis_moe_gemv(table, routed, x, False)
+    ws = torch.zeros(table.workspace_bytes(4), dtype=torch.uint8, device="cuda")
+    y = tb.trellis_moe_gemv(table, routed, x, False, ws=ws)
     torch.cuda.synchronize()
     yn = y.cpu().numpy()
     assert np.all(yn[1] == 0) and np.all(yn[2] == 0)
     assert np.any(yn[0] != 0) and np.any(yn[3] != 0)
-    assert tb.moe_error_word() != 0
+    assert int(ws[:4].view(torch.int32).item()) != 0
 
 
 def test_moe_glm_like_full_size():

@@ -311,6 +311,14 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
   const int in = P.L.in_features;
   const uint16_t *xp = P.L.x + (P.L.x_per_problem ? (size_t)p * B * in : (size_t)0);
 
+  // The workgroup's first copy goes out before the rest of the set-up (priority
+  // thresholds, sub-range bookkeeping, lane constants): its address needs only the first
+  // unit's (I, J).
+  if (fresh) {
+    const int I0 = __builtin_amdgcn_readfirstlane(first % nI), J0 = __builtin_amdgcn_readfirstlane(first / nI);
+    dma_unit<K>(code + (size_t)I0 * row_block_words + (size_t)(8 * J0) * NW, row_stride, ring, true);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   floatx4 acc[8];
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -353,7 +361,8 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
       dma_unit<K>(real ? nxt : code, row_stride, ring + j * (RG::UNIT_BYTES / 4), real);
       if (real) advance();
     };
-    prime(0);
+    if (fresh && sb == 0) advance();  // (its copy was issued above)
+    else prime(0);
     if (sb == 0) set_priority(prio_at(ub));  // (after the first copy is on its way)
     // Rotation loads: straight-line code (tasks past the last are clamped to it and their
     // values ignored), so all of them are in flight together.
