@@ -521,7 +521,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the kernels run on one GPU's share; sharding is described in DESIGN.md)", file=sys.stderr)
+              f"(the kernels run one GPU's share of a sharded layer)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -50,7 +50,7 @@ typedef enum {
   TRELLIS_EINVAL = -1,      /* bad size, K, cb, batch, side flag or NULL required pointer */
   TRELLIS_EALIGN = -2,      /* a pointer is not aligned as required */
   TRELLIS_EWORKSPACE = -3,  /* workspace NULL or smaller than trellis_workspace_bytes() */
-  TRELLIS_EUNSUPPORTED = -4,/* valid request this build does not implement */
+  TRELLIS_EUNSUPPORTED = -4,/* valid request that this library does not implement */
   TRELLIS_EHIP = -5         /* a HIP runtime call failed; see trellis_last_error() */
 } trellis_status;
 

@@ -4,7 +4,7 @@ import torch
 
 from trellis_coded_bit_amd import binding as tb
 
-# Spec tolerance for floating-point outputs: relative L2 over the whole output tensor.
+# Tolerance for floating-point outputs: relative L2 over the whole output tensor.
 REL_L2_TOL = 2e-3
 
 
