@@ -506,13 +506,49 @@ def run_encode(args, torch, tb, synth):
     return out
 
 
+def run_kernels(args, torch, tb, synth):
+    """The standalone entry points on the prefill matrix (K3 5120x17408) and activation
+    shape (2048 x 5120), each against HBM: algorithmic bytes (read + written) per call."""
+    wl = synth.prefill(args.seed)
+    lin = wl.layers["w"]
+    code = torch.from_numpy(lin.code).cuda()
+    x = torch.from_numpy(wl.xs["w"]).cuda()
+    r = torch.from_numpy(lin.rin).cuda()
+    sc = torch.from_numpy(lin.s_in).cuda()
+    y = torch.empty_like(x)
+
+    def timed(fn, n=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(n):
+            fn()
+        e0.record()
+        torch.cuda.synchronize()
+        return s0.elapsed_time(e0) / n
+
+    out = {"workload": "standalone entry points: decode of K3 5120x17408 tiles; had128_scale of fp16 [2048, 5120]"}
+    code_b = lin.code_bytes
+    for name, fn, nbytes in [
+        ("trellis_decode_tiles", lambda: tb.trellis_decode_tiles(code, lin.K), code_b + 5120 * 17408 * 2),
+        ("trellis_decode_tiles_e4m3", lambda: tb.trellis_decode_tiles_e4m3(code, lin.K), code_b + 5120 * 17408),
+        ("had128_scale", lambda: tb.had128_scale(x, r, sc, out=y), 2 * x.numel() * 2 + 5120 * 6),
+    ]:
+        ms = timed(fn)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "bytes": nbytes, "GBps": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--workload", default="dense", choices=["dense", "small_batch", "moe", "moe_mlp", "prefill", "encode"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "small_batch", "moe", "moe_mlp", "prefill", "encode", "kernels"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-unfused", action="store_true", help="moe_mlp: time only the fused call")
@@ -549,6 +585,8 @@ def main():
         print(json.dumps(run_moe_mlp(args, torch, tb, synth)), flush=True)
     elif args.workload == "encode":
         print(json.dumps(run_encode(args, torch, tb, synth)), flush=True)
+    elif args.workload == "kernels":
+        print(json.dumps(run_kernels(args, torch, tb, synth)), flush=True)
     else:
         print(json.dumps(run_prefill(args, torch, tb, synth)), flush=True)
         print(json.dumps(run_prefill(args, torch, tb, synth, fp8=True)), flush=True)
