@@ -131,7 +131,7 @@ int trellis_gemm(const trellis_linear *L, const uint16_t *x, int M, uint16_t *y,
 /* Decode to E4M3 bytes (the cb = 2 weights): w8[16i + r][16j + c] = the E4M3 code of
  * tile (i, j)'s element (r, c), i.e. the MCG codebook value rounded to E4M3.  Bit-exact.
  * ("EXLR8" page, E4M3 paragraph: EXL3's decode followed by the E4M3 rounding.)
- * code: int16 [in/16][out/16][16*K], 16-byte aligned; w8: uint8 out [in][out], 8-byte
+ * code: int16 [in/16][out/16][16*K], 16-byte aligned; w8: uint8 out [in][out], 16-byte
  * aligned.  in, out multiples of 16 (0 is a no-op). */
 int trellis_decode_tiles_e4m3(const int16_t *code, int K, int in_features, int out_features, uint8_t *w8,
                               void *stream);

@@ -182,7 +182,7 @@ def test_fp8_entry_validation(L):
     assert f(0x10000, 2, 60, 64, 0x20000, None) == EINVAL
     assert f(0x10000, 2, 0, 64, 0x20000, None) == 0
     assert f(0x10008, 2, 64, 64, 0x20000, None) == EALIGN
-    assert f(0x10000, 2, 64, 64, 0x20004, None) == EALIGN
+    assert f(0x10000, 2, 64, 64, 0x20008, None) == EALIGN
     assert f(0x10000, 2, 64, 64, None, None) == EINVAL
 
 

@@ -113,3 +113,27 @@ def test_workspace_too_small_launches_nothing():
     assert st == -3
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
+
+
+@pytest.mark.parametrize("post", [False, True])
+def test_had128_scale_unaligned_operands(post):
+    """Operands only 2-byte aligned take the per-element kernel; both kernels agree with the
+    oracle (and 5 x 3 blocks leave a partial group of the vectorised kernel)."""
+    rng = np.random.default_rng(7)
+    rows, n = 5, 384
+    x = rng.standard_normal((rows, n)).astype(np.float16)
+    r = rng.uniform(0.5, 1.5, n).astype(np.float16)
+    s = rng.normal(1, 0.02, n).astype(np.float32)
+    sc = O.side_scale(r, s)
+    ref = O.had_blocks(x.astype(np.float64)) * sc if post else O.had_blocks(x.astype(np.float64) * sc)
+    buf = torch.empty(rows * n + 1, dtype=torch.float16, device="cuda")
+    xu = buf[1:].view(rows, n)
+    xu.copy_(to_dev(x))
+    ybuf = torch.empty(rows * n + 1, dtype=torch.float16, device="cuda")
+    yu = ybuf[1:].view(rows, n)
+    tb.had128_scale(xu, to_dev(r), to_dev(s), post=post, out=yu)
+    ya = tb.had128_scale(to_dev(x), to_dev(r), to_dev(s), post=post)
+    torch.cuda.synchronize()
+    for y in (yu, ya):
+        got = y.cpu().numpy().astype(np.float64)
+        assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-3

@@ -193,7 +193,7 @@ int trellis_decode_tiles_e4m3(const int16_t *code, int K, int in_features, int o
                 out_features);
   if ((long long)in_features * out_features == 0) return TRELLIS_OK;
   if (!code || !w8) return fail(TRELLIS_EINVAL, "code or w8 is NULL");
-  if (!aligned(code, 16) || !aligned(w8, 8)) return fail(TRELLIS_EALIGN, "code must be 16-byte and w8 8-byte aligned");
+  if (!aligned(code, 16) || !aligned(w8, 16)) return fail(TRELLIS_EALIGN, "code and w8 must be 16-byte aligned");
   return hip_status(trellis::launch_decode_tiles_e4m3(code, K, in_features, out_features, w8, as_stream(stream)),
                     "trellis_decode_tiles_e4m3 launch");
 }

@@ -63,21 +63,22 @@ __global__ __launch_bounds__(256) void decode_tiles_kernel(const uint32_t *__res
 }
 
 // The E4M3 codebook variant ("EXLR8" page, E4M3 paragraph): the same decode, each value
-// rounded to E4M3 and written as one byte.  Workgroup per (tile row i, 8 tile columns) as
-// above; the 16 x 128 bytes are staged in LDS and written as 8 bytes per thread.
+// rounded to E4M3 and written as one byte.  Workgroup per (tile row i, 16 tile columns),
+// each wave decoding four tiles; the 16 x 256 bytes are staged in LDS and written as 16
+// bytes per thread.
 template <int K>
 __global__ __launch_bounds__(256) void decode_tiles_e4m3_kernel(const uint32_t *__restrict__ code, int Tj,
                                                                 uint8_t *__restrict__ w8, int out_features) {
   constexpr int NW = 8 * K;
-  __shared__ __attribute__((aligned(8))) uint8_t stage[16][128 + 8];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[16][256 + 16];
   const int i = blockIdx.y;
-  const int j0 = blockIdx.x * 8;
+  const int j0 = blockIdx.x * 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const LaneWindow lw = lane_window(lane, K);
   const int n = lane & 15;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int jj = 2 * wave + t;
+  for (int t = 0; t < 4; ++t) {
+    const int jj = 4 * wave + t;
     const int j = j0 + jj;
     if (j < Tj) {
       const uint32_t *tile = code + ((size_t)i * Tj + j) * NW;
@@ -90,17 +91,17 @@ __global__ __launch_bounds__(256) void decode_tiles_e4m3_kernel(const uint32_t *
   }
   __syncthreads();
   const int row = threadIdx.x >> 4, chunk = threadIdx.x & 15;
-  const int col = 16 * j0 + 8 * chunk;
+  const int col = 16 * j0 + 16 * chunk;
   if (col < out_features)
-    *reinterpret_cast<uint2 *>(w8 + (size_t)(16 * i + row) * out_features + col) =
-        *reinterpret_cast<const uint2 *>(&stage[row][8 * chunk]);
+    *reinterpret_cast<u32x4 *>(w8 + (size_t)(16 * i + row) * out_features + col) =
+        *reinterpret_cast<const u32x4 *>(&stage[row][16 * chunk]);
 }
 
 hipError_t launch_decode_tiles_e4m3(const int16_t *code, int K, int in_features, int out_features, uint8_t *w8,
                                     hipStream_t stream) {
   const int Ti = in_features / 16, Tj = out_features / 16;
   if (Ti == 0 || Tj == 0) return hipSuccess;
-  dim3 grid((Tj + 7) / 8, Ti), block(256);
+  dim3 grid((Tj + 15) / 16, Ti), block(256);
   const uint32_t *c = reinterpret_cast<const uint32_t *>(code);
   switch (K) {
     case 2: decode_tiles_e4m3_kernel<2><<<grid, block, 0, stream>>>(c, Tj, w8, out_features); break;
