@@ -400,7 +400,7 @@ def run_moe(args, torch, tb, synth):
             "code_bytes_per_token": nb, "code_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
 
 
-def run_moe_mlp(args, torch, tb, synth):
+def run_moe_mlp(args, torch, tb, synth, cb=1):
     """The fused routed-expert MLP of one token (trellis_moe_mlp): gate/up over 16 per-half
     slices of each of the 8 routed experts, silu(g) * u, down, router-weighted sum with one
     output rotation.  Routes and router weights re-drawn every token over 256 experts.  The
@@ -408,6 +408,10 @@ def run_moe_mlp(args, torch, tb, synth):
     activation and the weighted sum as torch ops) is timed beside it."""
     layer = synth.moe_mlp_layer(args.seed)
     E, H = len(layer.down), layer.halves
+    if cb != 1:  # the same codes read through the E4M3 codebook (the EXLR8 experts' format)
+        for e in range(E):
+            for l in layer.gate[e] + layer.up[e] + [layer.down[e]]:
+                l.cb = cb
     tables = tb.MoEMLPTables.from_host(layer)
     n_tok = args.warmup + args.steps + 64
     routes = synth.moe_routes(args.seed, n_tok)
@@ -443,7 +447,7 @@ def run_moe_mlp(args, torch, tb, synth):
         torch.mm(w_dev[i][None, :].half(), y_d, out=y.view(1, -1))
 
     res = {}
-    variants = (("fused", step),) if args.no_unfused else (("fused", step), ("unfused", step_unfused))
+    variants = (("fused", step),) if (args.no_unfused or cb != 1) else (("fused", step), ("unfused", step_unfused))
     for name, fn in variants:
         for i in range(64):  # warm-up tokens route across most of the 256 experts
             fn(i)
@@ -466,7 +470,8 @@ def run_moe_mlp(args, torch, tb, synth):
     ms = res["fused"]
     return {"workload": "fused routed-expert MLP decode (trellis_moe_mlp), 8 of 256 GLM-like experts, hidden 6144, "
                         "intermediate 2048 as 16 gate/up halves per expert with per-half K in {2,3,4}, down K per "
-                        "expert; routes and router weights re-drawn every token; 16 tokens per HIP graph",
+                        "expert; routes and router weights re-drawn every token; 16 tokens per HIP graph; "
+                        + ("MCG codebook" if cb == 1 else "E4M3 codebook (cb=2)"),
             "ms_per_token": round(ms, 5), "code_bytes_per_token": nb, "code_GBps": round(nb / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "unfused_ms_per_token": round(res["unfused"], 5) if "unfused" in res else None, "tokens_timed": steps}
@@ -583,6 +588,7 @@ def main():
         print(json.dumps(run_moe(args, torch, tb, synth)), flush=True)
     elif args.workload == "moe_mlp":
         print(json.dumps(run_moe_mlp(args, torch, tb, synth)), flush=True)
+        print(json.dumps(run_moe_mlp(args, torch, tb, synth, cb=2)), flush=True)
     elif args.workload == "encode":
         print(json.dumps(run_encode(args, torch, tb, synth)), flush=True)
     elif args.workload == "kernels":
