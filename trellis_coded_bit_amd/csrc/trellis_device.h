@@ -41,13 +41,17 @@ __device__ __forceinline__ _Float16 mcg_value(uint32_t h) {
 }
 
 // Codebook values of two hash words as an fp16 pair (a in the low half, b in the high
-// half): the lo and hi halves are gathered into two registers and added as packed fp16, one
-// round-to-nearest-even per value.
+// half), one round-to-nearest-even per value.  Each value is one fp16 add of a word's two
+// halves with SDWA operand selects; the second writes the high half and keeps the low one.
+// Two instructions per pair, against two v_perm_b32 and a packed add when the halves are
+// gathered first.
 __device__ __forceinline__ uint32_t mcg_value2(uint32_t a, uint32_t b) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x05040100u);  // (a.lo, b.lo)
-  const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07060302u);  // (a.hi, b.hi)
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, lo) + __builtin_bit_cast(h2, hi));
+  uint32_t r;
+  asm("v_add_f16_sdwa %0, %1, %1 dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:WORD_1"
+      : "=v"(r) : "v"(a));
+  asm("v_add_f16_sdwa %0, %1, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_0 src1_sel:WORD_1"
+      : "+v"(r) : "v"(b));
+  return r;
 }
 
 // The E4M3 codebook ("EXLR8" page, E4M3 paragraph: every codebook value is rounded to E4M3,
