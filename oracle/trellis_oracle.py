@@ -318,7 +318,20 @@ def forward(code: np.ndarray, K: int, rin, rout, s_in, s_out, x: np.ndarray,
     """
     code = np.asarray(code)
     Ti, Tj, _ = code.shape
-    n_in = 16 * Ti
+    if col_blocks is None:
+        cols = np.arange(Tj)
+    else:
+        cols = np.concatenate([np.arange(8 * J, 8 * J + 8) for J in col_blocks])
+    sub = code[:, cols, :]
+    chunks = (decode_tiles(sub[a:a + row_chunk], K, cb) for a in range(0, Ti, row_chunk))
+    ch = np.concatenate([np.arange(16 * j, 16 * j + 16) for j in cols])
+    return _forward_rows(chunks, 16 * Ti, rin, s_in, np.asarray(rout)[ch],
+                         None if s_out is None else np.asarray(s_out)[ch], x, act_e4m3)
+
+
+def _forward_rows(w_chunks, n_in, rin, s_in, rout, s_out, x, act_e4m3):
+    """The forward of the reconstruction paragraph with W_hat given as consecutive blocks of
+    rows (decoded fp16 values, a multiple of 128 rows each except the last)."""
     x = np.atleast_2d(np.asarray(x)).astype(np.float64)
     assert x.shape[1] == n_in
     su = side_scale(rin, s_in)
@@ -329,18 +342,25 @@ def forward(code: np.ndarray, K: int, rin, rout, s_in, s_out, x: np.ndarray,
         amax = np.max(np.abs(xh), axis=1)
         sc = amax / E4M3_MAX
         xh = np.where(amax[:, None] > 0, e4m3_round(xh / np.where(amax > 0, sc, 1.0)[:, None]), 0.0)
-    if col_blocks is None:
-        cols = np.arange(Tj)
-    else:
-        cols = np.concatenate([np.arange(8 * J, 8 * J + 8) for J in col_blocks])
-    sub = code[:, cols, :]
-    y_pre = np.zeros((x.shape[0], 16 * len(cols)))
-    for a in range(0, Ti, row_chunk):
-        w = decode_tiles(sub[a:a + row_chunk], K, cb).astype(np.float64)
-        y_pre += xh[:, 16 * a:16 * a + w.shape[0]] @ w
+    y_pre, a = None, 0
+    for w in w_chunks:
+        w = np.asarray(w).astype(np.float64)
+        part = xh[:, a:a + w.shape[0]] @ w
+        y_pre = part if y_pre is None else y_pre + part
+        a += w.shape[0]
+    assert a == n_in
     y_pre *= sc[:, None]
-    ch = np.concatenate([np.arange(16 * j, 16 * j + 16) for j in cols])
-    return had_blocks(y_pre) * sv[ch]
+    return had_blocks(y_pre) * sv
+
+
+def forward_decoded(w_hat: np.ndarray, rin, rout, s_in, s_out, x: np.ndarray, row_chunk: int = 1024,
+                    act_e4m3: bool = False) -> np.ndarray:
+    """forward() with the matrix already decoded: w_hat fp16 [in, out] = decode_tiles(code),
+    so that one decode serves several inputs.  Same definition, same float64 arithmetic
+    (the product is taken over blocks of row_chunk input rows and the blocks summed)."""
+    w_hat = np.asarray(w_hat)
+    chunks = (w_hat[a:a + row_chunk] for a in range(0, w_hat.shape[0], row_chunk))
+    return _forward_rows(chunks, w_hat.shape[0], rin, s_in, rout, s_out, x, act_e4m3)
 
 
 def forward_linear(lin, x, col_blocks=None, act_e4m3: bool = False) -> np.ndarray:

@@ -1,9 +1,9 @@
 """Pins for the CPU oracle against what the pages and mathematics fix (no GPU needed).
 
 Each test names the fact it checks and where the fact comes from.  The oracle is never
-checked against itself: each pin uses a second route (a hand derivation, the printed K=2
-decoder rule, the public PTX fragment layout, scipy, Python's own binary16 packing, the
-rate-distortion bound, or an encoder round trip).
+checked against itself: each pin uses a second route (a hand derivation, the public PTX
+fragment layout, scipy, Python's own binary16 packing, the rate-distortion bound, or an
+encoder round trip).
 """
 import math
 import os
@@ -84,35 +84,34 @@ def test_codebook_statistics_match_codebook_scale():
 # Bit layout
 # ---------------------------------------------------------------------------------------
 
-def _k2_states_by_lane_rule(words: np.ndarray) -> np.ndarray:
-    """K=2 states from the lane rule in [ESCHA] "Bit layout" (pure Python, one tile).
-
-    A 32-lane decoder gives lane L the symbols 8L..8L+7.  The lane forms a 64-bit value from
-    the previous 32-bit word (circularly) above the current word (word index (8L)>>4), moves
-    it right by 16 bits when bit 3 of 8L is clear, and takes symbol 8L+j's state as the 16
-    bits starting at bit 14-2j.
-    """
-    w = [int(v) & 0xFFFF for v in words]
-    u32 = [w[2 * i] | (w[2 * i + 1] << 16) for i in range(16)]
-    st = [0] * 256
-    for L in range(32):
-        t0 = 8 * L
-        cur = t0 >> 4
-        prev = (cur + 15) & 15
-        b = (u32[prev] << 32) | u32[cur]
-        if (t0 & 8) == 0:
-            b >>= 16
-        for j in range(8):
-            st[t0 + j] = (b >> (14 - 2 * j)) & 0xFFFF
-    return np.array(st, np.uint16)
+def test_states_hand_derived_tiles():
+    """tests/golden/states_hand.txt: tiles with one non-zero symbol, their states derived by
+    hand from the bit-layout definition (word pairing, most-significant-bit-first stream,
+    window ending at the symbol's own K bits, circular) at K = 2, 3, 4."""
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "states_hand.txt")) if l.strip() and not l.startswith("#")]
+    assert len(rows) == 3
+    for K_s, words_s, states_s in rows:
+        K = int(K_s)
+        w = np.zeros((1, 16 * K), np.uint16)
+        for item in words_s.split(","):
+            i, v = item.split("=")
+            w[0, int(i)] = int(v, 16)
+        expect = np.zeros(256, np.int64)
+        for item in states_s.split(","):
+            i, v = item.split("=")
+            expect[int(i)] = int(v, 16)
+        got = O.tile_states(w.view(np.int16), K)[0].astype(np.int64)
+        np.testing.assert_array_equal(got, expect, err_msg=f"K={K}")
 
 
-def test_k2_states_match_printed_lane_rule():
-    rng = np.random.default_rng(11)
-    code = _rand_code(rng, 40, 2)
-    ours = O.tile_states(code, 2)
-    for t in range(code.shape[0]):
-        np.testing.assert_array_equal(ours[t], _k2_states_by_lane_rule(code[t]))
+def test_states_catch_swapped_word_halves():
+    """The hand-derived case discriminates the pairing order: putting the set half in the
+    other half of its 32-bit word (big-endian pairing) moves the symbol and changes the
+    states (shown by decoding the swapped tile with the oracle)."""
+    w = np.zeros((1, 32), np.uint16)
+    w[0, 2] = 0x2000  # the golden K = 2 case's half in the wrong position
+    st = O.tile_states(w.view(np.int16), 2)[0]
+    assert st[17] == 0 and st[24] == 0 and np.count_nonzero(st) > 0
 
 
 def test_states_special_streams():
@@ -502,6 +501,64 @@ def test_moe_mlp_equals_dense_composition():
         assert O.rel_l2(act[k], a[0]) < 1e-12
         ref += w[k] * (a @ Wd)
     assert O.rel_l2(y, ref[0]) < 1e-12
+
+
+def _small_moe(seed=0):
+    """A 4-expert MoE layer at hidden 256 / inner 128 whose per-expert hidden-side vectors
+    (which moe_forward must NOT use) differ from the shared ones."""
+    return synth.moe_layer(seed, n_experts=4, hidden=256, inner=128)
+
+
+def test_moe_forward_equals_dense_matrices():
+    """[EXLR8] shared-rotation paragraph: every expert's hidden side uses the layer's one
+    vector pair.  Per routed expert, gate/up outputs equal x Wg and x Wu and the down output
+    x_k Wd, with dense matrices built independently (scipy's Hadamard, _dense) from each
+    expert's code: gate/up with the SHARED hidden input vectors on the input side and the
+    expert's own on the 128-wide output side; down with the expert's own input vectors and
+    the SHARED hidden output vectors."""
+    L = _small_moe(0)
+    routed = [3, 1, 2]
+    x = synth.make_x(np.random.SeedSequence(21), 1, 256)
+    xd = synth.make_x(np.random.SeedSequence(22), 3, 128)
+    g, u, d = O.moe_forward(L, routed, x, xd)
+    xf, xdf = x.astype(np.float64), xd.astype(np.float64)
+    for k, e in enumerate(routed):
+        ge, ue, de = L.gate[e], L.up[e], L.down[e]
+        Wg = _dense(ge, L.r_hidden_in, L.s_hidden_in, ge.rout, ge.s_out)
+        Wu = _dense(ue, L.r_hidden_in, L.s_hidden_in, ue.rout, ue.s_out)
+        Wd = _dense(de, de.rin, de.s_in, L.r_hidden_out, L.s_hidden_out)
+        assert O.rel_l2(g[k], (xf @ Wg)[0]) < 1e-12
+        assert O.rel_l2(u[k], (xf @ Wu)[0]) < 1e-12
+        assert O.rel_l2(d[k], (xdf[k:k + 1] @ Wd)[0]) < 1e-12
+
+
+def test_moe_forward_pin_catches_swapped_side_vectors():
+    """The pin above discriminates: had moe_forward used the experts' own hidden-side vectors
+    instead of the shared ones (or swapped which side is shared), its outputs would differ
+    from the dense reference by far more than rounding."""
+    L = _small_moe(1)
+    e = 2
+    x = synth.make_x(np.random.SeedSequence(23), 1, 256)
+    xd = synth.make_x(np.random.SeedSequence(24), 1, 128)
+    g, _, d = O.moe_forward(L, [e], x, xd)
+    ge, de = L.gate[e], L.down[e]
+    wrong_in = _dense(ge, ge.rin, ge.s_in, ge.rout, ge.s_out)              # per-expert hidden input side
+    wrong_side = _dense(ge, L.r_hidden_in, L.s_hidden_in, L.r_hidden_out[:128], L.s_hidden_out[:128])
+    wrong_out = _dense(de, de.rin, de.s_in, de.rout, de.s_out)             # per-expert hidden output side
+    xf = x.astype(np.float64)
+    assert O.rel_l2(g[0], (xf @ wrong_in)[0]) > 0.05
+    assert O.rel_l2(g[0], (xf @ wrong_side)[0]) > 0.05
+    assert O.rel_l2(d[0], (xd.astype(np.float64) @ wrong_out)[0]) > 0.05
+
+
+def test_forward_decoded_is_forward():
+    """forward_decoded(decode_tiles(code)) is forward(code): the same definition evaluated
+    in the same float64 order (a refactoring check)."""
+    lin = synth.make_linear(np.random.SeedSequence(31), 3, 2048, 384)
+    x = synth.make_x(np.random.SeedSequence(32), 3, 2048)
+    a = O.forward_linear(lin, x)
+    b = O.forward_decoded(O.decode_tiles(lin.code, 3), lin.rin, lin.rout, lin.s_in, lin.s_out, x)
+    np.testing.assert_array_equal(a, b)
 
 
 def test_moe_mlp_halves_are_consecutive_channel_slices():
