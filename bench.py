@@ -1,14 +1,18 @@
 """Benchmark of the trellis-coded GEMV hot path on one MI355X.
 
 Default workload: the dense-MLP decode step at batch 1 (gate K2 5120->17408, up K3
-5120->17408, down K3 17408->5120), i.e. three fused trellis_gemv launches per step.
-Metric: code bytes (in*out*K/8 summed over the three matrices) per second.
+5120->17408, down K3 17408->5120, each on its own input), one trellis_gemv_list launch per
+step.  Metric: code bytes (in*out*K/8 summed over the three matrices) per second.  The same
+JSON line carries the single-matrix latency, the small-batch decode at B = 1, 2, 4, 8, the
+MoE decode (8 of 256 experts), fp16 and FP8 prefill, the roofline of the step's kernel
+against HBM with the measured decode ceiling beside it, and the CPU oracle timed on a
+bounded sample.
 
 Weights are rotated over enough distinct device copies (> 1 GiB in total) that the 256 MB
 Infinity Cache cannot serve them between steps; inputs are resident in HBM before timing.
 
-Prints ONE JSON line (rank 0, N = 1).  Extra workloads (small-batch, MoE, the fused
-routed-expert MLP, prefill) are available with --workload for separate measurement lines.
+Prints ONE JSON line (rank 0, N = 1).  --workload selects the other lines (the fused
+routed-expert MLP, the encoder, the standalone entry points, the microbenchmarks).
 """
 from __future__ import annotations
 
@@ -27,10 +31,6 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 MFMA_F8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
-# Vector-ALU bound of the codebook decode: 1024 SIMDs at 2.4 GHz; per wave64 of 4 weights
-# per lane (256 weights) the hash needs 4 window extractions and 4 32-bit multiplies (half
-# lane rate: 4 clocks each) and 4 mask-xors (full rate: 2 clocks each) = 40 clocks.
-DECODE_PEAK_WEIGHTS_PER_S = 1024 * 2.4e9 * 256 / 40
 ROTATE_BYTES = 1 << 30
 COPY_PROBE_BYTES = 256 << 20   # plain device copy used to calibrate the HBM byte counters
 # Counter-derived HBM traffic of the GEMV launch, with the hash of the kernel sources it was
@@ -180,97 +180,132 @@ class LayerStack:
             self._graph(n % self.R).replay()
 
 
-def run_dense(args, torch, tb, synth):
-    """The dense-MLP decode step: gate and up share their input, so they run as one launch
-    over a two-entry layer table (trellis_moe_gemv, per-entry K); down is one trellis_gemv."""
-    wl = synth.dense_mlp(args.seed, batch=1)
-    names = ["gate", "up", "down"]
-    code_bytes = sum(wl.layers[n].code_bytes for n in names)
-    gu_bytes = wl.layers["gate"].code_bytes + wl.layers["up"].code_bytes
-    flops = sum(2 * wl.layers[n].in_features * wl.layers[n].out_features for n in names)
-    R = _copies(code_bytes)
-    _log(f"dense MLP: {code_bytes / 1e6:.2f} MB code per step, {R} weight copies")
-    base = {n: tb.TrellisLinear.from_host(wl.layers[n]) for n in names}
-    copies = [base] + [{n: tb.TrellisLinear(base[n].code.clone(), base[n].rin, base[n].rout, base[n].s_in,
-                                            base[n].s_out, base[n].K) for n in names} for _ in range(R - 1)]
-    tables = [tb.ExpertTable([c["gate"], c["up"]]) for c in copies]
-    routed = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
-    assert np.array_equal(wl.xs["gate"], wl.xs["up"])
-    x_gu = torch.from_numpy(wl.xs["gate"][0]).cuda()
-    x_d = torch.from_numpy(wl.xs["down"]).cuda()
-    y_gu = torch.empty((2, 17408), dtype=torch.float16, device="cuda")
-    y_d = torch.empty((1, 5120), dtype=torch.float16, device="cuda")
-    nb = max(base["down"].workspace_bytes(tb.TRELLIS_OP_GEMV, 1), tables[0].workspace_bytes(2))
-    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+def _per_launch_us(torch, fn, R, reps):
+    """Average duration of one launch: a HIP graph of R back-to-back launches (one per
+    weight copy), replayed `reps` times between HIP events on the capturing stream's
+    successor (the events see the launches' own stream: the replays run on it)."""
+    g = _capture(torch, lambda: [fn(i) for i in range(R)])
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * R)
 
-    def gate_up(i):
-        tb.trellis_moe_gemv(tables[i % R], routed, x_gu, False, out=y_gu, ws=ws)
 
-    def down(i):
-        tb.trellis_gemv(copies[i % R]["down"], x_d, out=y_d, ws=ws)
-
-    def step(i):
-        gate_up(i)
-        down(i)
-
-    # eager warm-up, then HIP graphs of consecutive steps over the weight copies (R steps per
-    # graph: the MLPs of R layers in a row, as in one captured decode pass of a model)
+def _time_steps(torch, step, R, warmup, steps):
+    """Eager warm-up over the weight copies, then HIP graphs of consecutive steps (R steps
+    per graph, as the layers of a captured decode pass follow one another); exactly `steps`
+    timed.  Returns ms per step."""
     for i in range(R):
         step(i)
     torch.cuda.synchronize()
     stack = LayerStack(torch, step, R)
-    stack.prepare(args.warmup, args.steps)
-    stack.run(args.warmup)
+    stack.prepare(warmup, steps)
+    stack.run(warmup)
     torch.cuda.synchronize()
     t_s = torch.cuda.Event(enable_timing=True)
     t_e = torch.cuda.Event(enable_timing=True)
     t_s.record()
-    stack.run(args.steps)
+    stack.run(steps)
     t_e.record()
     torch.cuda.synchronize()
-    ms_step = t_s.elapsed_time(t_e) / args.steps
-    # per-launch duration of each launch (its two kernels): a graph of R back-to-back launches
-    launch_us = {}
-    for name, fn in [("gate_up", gate_up), ("down", down)]:
-        g = _capture(torch, lambda fn=fn: [fn(i) for i in range(R)])
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = max(2, args.steps // R)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        launch_us[name] = e0.elapsed_time(e1) * 1e3 / (reps * R)
-    # the dominant kernel: the gate+up launch (the larger share of the step)
-    achieved = gu_bytes / (launch_us["gate_up"] * 1e-6) / 1e9
-    gu_weights = sum(wl.layers[n].in_features * wl.layers[n].out_features for n in ("gate", "up"))
-    alu_peak_gbs = DECODE_PEAK_WEIGHTS_PER_S * (gu_bytes / gu_weights) / 1e9
+    return t_s.elapsed_time(t_e) / steps
+
+
+def _weight_copies(tb, base, R):
+    """R distinct device copies of the layers' codes (side vectors shared)."""
+    return [base] + [{n: tb.TrellisLinear(l.code.clone(), l.rin, l.rout, l.s_in, l.s_out, l.K, l.cb)
+                      for n, l in base.items()} for _ in range(R - 1)]
+
+
+def decode_ceiling(tb, weights_per_code_byte):
+    """The decode's vector-instruction ceiling, measured: the products' per-tile decode and
+    MFMA sequence (trellis_micro_valu, 4 waves per SIMD, as the products run) in tiles per
+    second for the whole chip, in code bytes per second of the given width mix."""
+    tb.micro_clock_kernel("valu", "decode_tile_mfma", 4, 4)
+    cyc, tick, ms = tb.micro_clock_kernel("valu", "decode_tile_mfma", 4000, 4)
+    tiles = 4 * tb.micro_cus() * 4 * 4000 * 16  # SIMDs x waves per SIMD x iterations x tiles
+    ghz = float((cyc.double() / (tick.double() * 10.0)).median())
+    tiles_per_s = tiles / (ms * 1e-3)
+    simds = 4 * tb.micro_cus()
+    return {"GBps": round(tiles_per_s * 256 / weights_per_code_byte / 1e9, 1),
+            "clocks_per_tile_per_simd": round(simds * ghz * 1e9 / tiles_per_s, 2), "ghz": round(ghz, 3),
+            "method": "trellis_micro_valu decode_tile_mfma (K3 decode + one 16x16x32 MFMA per tile, LDS-resident "
+                      "words, 4 waves per SIMD), wall time"}
+
+
+def run_dense(args, torch, tb, synth):
+    """The dense-MLP decode step at batch 1: the workload's three matrices (gate K2, up K3,
+    down K3, each on its own input) as ONE trellis_gemv_list launch.  Beside it, the same
+    matrices as a dependent chain (gate+up one launch, then down), as a model's MLP runs."""
+    wl = synth.dense_mlp(args.seed, batch=1)
+    names = ["gate", "up", "down"]
+    code_bytes = sum(wl.layers[n].code_bytes for n in names)
+    weights = sum(wl.layers[n].in_features * wl.layers[n].out_features for n in names)
+    flops = 2 * weights
+    R = _copies(code_bytes)
+    _log(f"dense MLP: {code_bytes / 1e6:.2f} MB code per step, {R} weight copies")
+    base = {n: tb.TrellisLinear.from_host(wl.layers[n]) for n in names}
+    copies = _weight_copies(tb, base, R)
+    xs = [torch.from_numpy(wl.xs[n]).cuda() for n in names]
+    ys = [torch.empty((1, wl.layers[n].out_features), dtype=torch.float16, device="cuda") for n in names]
+    ws = torch.zeros(tb.trellis_gemv_list_workspace_bytes([base[n] for n in names], 1), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(i):
+        tb.trellis_gemv_list([copies[i % R][n] for n in names], xs, ys, ws=ws)
+
+    ms_step = _time_steps(torch, step, R, args.warmup, args.steps)
+    launch_us = _per_launch_us(torch, step, R, max(2, args.steps // R))
+
+    def chain(i):  # gate+up (shared x) in one launch, then down
+        c = copies[i % R]
+        tb.trellis_gemv_list([c["gate"], c["up"]], xs[:2], ys[:2], ws=ws)
+        tb.trellis_gemv_list([c["down"]], xs[2:], ys[2:], ws=ws)
+
+    ms_chain = _time_steps(torch, chain, R, args.warmup, args.steps)
+    achieved = code_bytes / (launch_us * 1e-6) / 1e9
     value = code_bytes / (ms_step * 1e-3) / 1e9
+    ceiling = decode_ceiling(tb, weights / code_bytes)
     out = {
         "metric": "trellis GEMV code-bytes GB/s (% HBM peak) at batch 1; prefill TFLOP/s",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp16", "data": "synthetic",
-        "config": {"workload": "dense MLP decode, batch 1: gate K2 5120x17408 + up K3 5120x17408 (one "
-                               "trellis_moe_gemv launch over a 2-entry table, shared x) + down K3 17408x5120 "
-                               "(trellis_gemv); steps over 13 weight copies captured as consecutive layers in HIP graphs",
+        "config": {"workload": "dense MLP decode, batch 1: gate K2 5120x17408 + up K3 5120x17408 + down K3 "
+                               "17408x5120, each on its own x, as one trellis_gemv_list launch per step; steps over "
+                               f"{R} weight copies captured as consecutive layers in HIP graphs",
                    "global_batch": 1, "code_bytes_per_step": code_bytes, "weight_copies_rotated": R,
                    "parallelism": "single GPU"},
-        # the launch is bound by the decode's vector-ALU work, not by HBM: its peak is the
-        # decode bound above, in code bytes per second for this launch's mix of widths
-        "roofline": {"bound": "alu", "achieved": round(achieved, 1), "peak": round(alu_peak_gbs, 1), "unit": "GB/s",
-                     "frac": round(achieved / alu_peak_gbs, 4), "traffic": measured_traffic()},
-        "roofline_hbm": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4)},
-        "roofline_kernel": "gate+up launch (gemv_partial_kernel + gemv_finish_kernel over 2 problems)",
-        "algorithmic_bytes_per_launch": gu_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic()},
+        "roofline_kernel": "gemv_kernel<list, mixed K> (the step's one launch)",
+        "algorithmic_bytes_per_launch": code_bytes,
+        "launch_us": round(launch_us, 2),
+        "decode_alu_ceiling": {**ceiling, "frac_of_it": round(achieved / ceiling["GBps"], 4)},
         "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
         "effective_weight_tflops": round(flops / (ms_step * 1e-3) / 1e12, 3),
-        "launch_us": {k: round(v, 2) for k, v in launch_us.items()},
+        "dependent_chain": {"ms_per_step": round(ms_chain, 5),
+                            "code_GBps": round(code_bytes / (ms_chain * 1e-3) / 1e9, 1),
+                            "what": "gate+up as one launch, then down (two launches), as in a model's MLP"},
     }
     return out, wl
+
+
+def run_single(args, torch, tb, synth):
+    """The single-matrix workload (K2 512 -> 256, s = 1): latency of one trellis_gemv."""
+    wl = synth.single_k2(args.seed)
+    lin = tb.TrellisLinear.from_host(wl.layers["w"])
+    x = torch.from_numpy(wl.xs["w"]).cuda()
+    y = torch.empty((1, lin.out_features), dtype=torch.float16, device="cuda")
+    ws = torch.zeros(lin.workspace_bytes(tb.TRELLIS_OP_GEMV, 1), dtype=torch.uint8, device="cuda")
+    us = _per_launch_us(torch, lambda i: tb.trellis_gemv(lin, x, out=y, ws=ws), 64, 20)
+    return {"workload": "single matrix K2 512x256, s = 1, batch 1 (trellis_gemv)", "us_per_call": round(us, 2),
+            "code_bytes": wl.layers["w"].code_bytes}
 
 
 def run_prefill(args, torch, tb, synth, fp8=False):
@@ -306,40 +341,27 @@ def run_prefill(args, torch, tb, synth, fp8=False):
 
 
 def run_small_batch(args, torch, tb, synth, B):
+    """Small-batch decode: the workload's three K2 matrices at batch B as one
+    trellis_gemv_list launch per step."""
     wl = synth.small_batch(args.seed, batch=B)
     names = ["qkv", "z", "out"]
     code_bytes = sum(wl.layers[n].code_bytes for n in names)
     R = _copies(code_bytes)
     base = {n: tb.TrellisLinear.from_host(wl.layers[n]) for n in names}
-    copies = [base] + [{n: tb.TrellisLinear(base[n].code.clone(), base[n].rin, base[n].rout, base[n].s_in,
-                                            base[n].s_out, base[n].K) for n in names} for _ in range(R - 1)]
-    xs = {n: torch.from_numpy(wl.xs[n]).cuda() for n in names}
-    ys = {n: torch.empty((B, wl.layers[n].out_features), dtype=torch.float16, device="cuda") for n in names}
-
-    nb = max(base[n].workspace_bytes(tb.TRELLIS_OP_GEMV, B) for n in names)
-    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    copies = _weight_copies(tb, base, R)
+    xs = [torch.from_numpy(wl.xs[n]).cuda() for n in names]
+    ys = [torch.empty((B, wl.layers[n].out_features), dtype=torch.float16, device="cuda") for n in names]
+    ws = torch.zeros(tb.trellis_gemv_list_workspace_bytes([base[n] for n in names], B), dtype=torch.uint8,
+                     device="cuda")
 
     def step(i):
-        for n in names:
-            tb.trellis_gemv(copies[i % R][n], xs[n], out=ys[n], ws=ws)
+        tb.trellis_gemv_list([copies[i % R][n] for n in names], xs, ys, ws=ws)
 
-    # HIP graphs of consecutive steps over the weight copies (as for the dense step)
-    for i in range(R):
-        step(i)
-    torch.cuda.synchronize()
-    stack = LayerStack(torch, step, R)
-    stack.prepare(args.warmup, args.steps)
-    stack.run(args.warmup)
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    stack.run(args.steps)
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / args.steps
-    return {"workload": f"small-batch decode K2 B={B} (qkv 5120x10240, z 5120x6144, out 6144x5120; "
-                        "three trellis_gemv per step; consecutive steps over the weight copies in HIP graphs)", "ms_per_step": round(ms, 5),
-            "code_GBps": round(code_bytes / (ms * 1e-3) / 1e9, 1),
+    ms = _time_steps(torch, step, R, args.warmup, args.steps)
+    gbs = code_bytes / (ms * 1e-3) / 1e9
+    return {"workload": f"small-batch decode K2 B={B} (qkv 5120x10240, z 5120x6144, out 6144x5120; one "
+                        "trellis_gemv_list launch per step; consecutive steps over the weight copies in HIP graphs)",
+            "B": B, "ms_per_step": round(ms, 5), "code_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "effective_weight_tflops": round(2 * B * sum(wl.layers[n].in_features * wl.layers[n].out_features
                                                        for n in names) / (ms * 1e-3) / 1e12, 3)}
 
@@ -396,8 +418,12 @@ def run_moe(args, torch, tb, synth):
     ms = s.elapsed_time(e) / (n_chunks * chunk)
     args = argparse.Namespace(**{**vars(args), "steps": n_chunks * chunk})
     nb = float(np.mean(bytes_tok[64:64 + args.steps]))
-    return {"workload": "MoE decode, 8 of 256 GLM-like experts, K in {2,3,4}", "ms_per_token": round(ms, 5),
-            "code_bytes_per_token": nb, "code_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {"workload": "MoE decode, 8 of 256 GLM-like experts, K in {2,3,4}: gate+up of the routed experts as one "
+                        "trellis_moe_gemv launch (16 products, shared rotated input), down as one (8 products); "
+                        "routes re-drawn every token; 16 tokens per HIP graph",
+            "ms_per_token": round(ms, 5), "code_bytes_per_token": nb, "code_GBps": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def run_moe_mlp(args, torch, tb, synth, cb=1):
@@ -547,15 +573,91 @@ def run_kernels(args, torch, tb, synth):
     return out
 
 
+def run_micro(args, torch, tb):
+    """The hardware ceilings: cold HBM stream read, vector-instruction issue costs of the
+    decode (single instructions and whole per-tile sequences), matrix-instruction rates.
+    Clocks are the shader clock (s_memtime); its frequency under each load is reported."""
+    out = {"workload": "microbenchmarks: HBM stream read, decode vector-instruction costs, MFMA rates"}
+    # cold stream read: 8 GiB (32x the Infinity Cache), 16-byte loads from every CU
+    nbytes = 8 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    tb.micro_stream_read(buf)
+    torch.cuda.synchronize()
+    rates = []
+    for blocks in (0, 2048, 4096):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(4):
+            tb.micro_stream_read(buf, blocks)
+        e1.record()
+        torch.cuda.synchronize()
+        rates.append((nbytes * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9, blocks))
+    best = max(rates)
+    out["hbm_stream_read_GBps"] = round(best[0], 1)
+    out["hbm_stream_read_frac_of_8TBps"] = round(best[0] / HBM_PEAK_GBS, 4)
+    out["hbm_stream_read_by_grid"] = {str(b or "8/CU"): round(r, 1) for r, b in rates}
+    del buf
+    torch.cuda.empty_cache()
+    _log(f"stream read {best[0]:.0f} GB/s")
+
+    simds = 4 * tb.micro_cus()
+
+    def clk(kind, name, iters, wps, per):
+        """Per SIMD: wall-clock ns per wave instruction (or tile) over the whole launch, and
+        that in shader clocks at the frequency measured in the kernel (s_memtime cycles over
+        the 100 MHz s_memrealtime ticks)."""
+        tb.micro_clock_kernel(kind, name, 4, wps)  # warm-up
+        cyc, tick, ms = tb.micro_clock_kernel(kind, name, iters, wps)
+        ghz = float((cyc.double() / (tick.double() * 10.0)).median())
+        per_simd = wps * iters * per  # wave instructions (or tiles) each SIMD executes
+        ns = ms * 1e6 / per_simd
+        return ns * ghz, ghz, ns
+
+    valu = {}
+    for name in tb.MICRO_VALU:
+        row = {}
+        for wps in (1, 2, 4, 8):
+            c, ghz, _ = clk("valu", name, 20000, wps, 64)
+            row[f"w{wps}"] = round(c, 3)
+        row["ghz"] = round(ghz, 3)
+        valu[name] = row
+    out["valu_clocks_per_wave_instruction_per_simd"] = valu
+    dec = {}
+    for name in tb.MICRO_DECODE:
+        row = {}
+        for wps in (1, 2, 4, 8):
+            c, ghz, _ = clk("valu", name, 4000, wps, 16)
+            row[f"w{wps}"] = round(c, 2)
+        row["ghz"] = round(ghz, 3)
+        dec[name] = row
+    out["decode_clocks_per_tile_per_simd"] = dec
+    mf = {}
+    for name, (_, macs) in tb.MICRO_MFMA.items():
+        row = {}
+        for wps in (1, 2, 4):
+            c, ghz, ns = clk("mfma", name, 4000, wps, 8)
+            row[f"w{wps}_clocks"] = round(c, 2)
+            row[f"w{wps}_tflops"] = round(2 * macs / ns * simds / 1e3, 1)
+            row[f"w{wps}_ghz"] = round(ghz, 3)
+        mf[name] = row
+    out["mfma"] = mf
+    out["cus"] = tb.micro_cus()
+    out["method"] = ("wall time of one launch (events) over the instructions each SIMD issues; clocks at "
+                     "the in-kernel s_memtime/s_memrealtime frequency")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--workload", default="dense", choices=["dense", "small_batch", "moe", "moe_mlp", "prefill", "encode", "kernels"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "small_batch", "moe", "moe_mlp", "prefill", "encode", "kernels", "micro"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="dense: skip the single, small-batch and MoE lines")
     ap.add_argument("--no-unfused", action="store_true", help="moe_mlp: time only the fused call")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
@@ -573,6 +675,11 @@ def main():
 
     if args.workload == "dense":
         out, wl = run_dense(args, torch, tb, synth)
+        if not args.no_extra:
+            out["single"] = run_single(args, torch, tb, synth)
+            out["small_batch"] = [run_small_batch(args, torch, tb, synth, B) for B in (1, 2, 4, 8)]
+            out["moe"] = run_moe(args, torch, tb, synth)
+            torch.cuda.empty_cache()
         if not args.no_prefill:
             out["prefill"] = run_prefill(args, torch, tb, synth)
             out["prefill_fp8"] = run_prefill(args, torch, tb, synth, fp8=True)
@@ -593,6 +700,8 @@ def main():
         print(json.dumps(run_encode(args, torch, tb, synth)), flush=True)
     elif args.workload == "kernels":
         print(json.dumps(run_kernels(args, torch, tb, synth)), flush=True)
+    elif args.workload == "micro":
+        print(json.dumps(run_micro(args, torch, tb)), flush=True)
     else:
         print(json.dumps(run_prefill(args, torch, tb, synth)), flush=True)
         print(json.dumps(run_prefill(args, torch, tb, synth, fp8=True)), flush=True)

@@ -27,11 +27,17 @@
  *   - Validation happens on the host BEFORE anything is enqueued.  A failed check returns a
  *     negative trellis_status and sets trellis_last_error(); nothing is launched.  A launch
  *     failure returns TRELLIS_EHIP with the HIP error text.  No exception crosses the ABI.
- *   - Workspaces are owned by the caller.  A workspace must be zero-filled before its first
- *     use; every call leaves its counters at zero again, so one workspace serves any number
- *     of back-to-back calls on ONE stream.  Calls that overlap in time (several streams)
- *     need separate workspaces.  trellis_gemm stores activations in its workspace, so a
- *     buffer used by trellis_gemm must be zero-filled again before a GEMV or MoE call uses it.
+ *   - Workspaces are owned by the caller, 256-byte aligned, and zero-filled before their
+ *     first use.  Every workspace starts with the same reserved region: bytes [0, 256) are a
+ *     header whose first uint32 is the ERROR WORD, and the next 64 KiB hold the small-batch
+ *     products' counters, which each call leaves at zero again and no entry point leaves
+ *     dirty.  So one zero-filled buffer, large enough for the largest request, serves any
+ *     number of back-to-back calls of every entry point, in any order, on ONE stream.
+ *     Calls that overlap in time (several streams) need separate workspaces.
+ *   - The error word is sticky: kernels only OR bits into it (1: a routed id out of range
+ *     or a table entry with an invalid K/cb was skipped; 2: a prefill workgroup's bounded
+ *     wait for another ran out).  The caller reads it and clears it by writing 0 to the
+ *     first 4 bytes of the workspace (any device fill, e.g. on the same stream).
  */
 #ifndef TRELLIS_H_
 #define TRELLIS_H_
@@ -43,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TRELLIS_ABI_VERSION 1
+#define TRELLIS_ABI_VERSION 2
 
 typedef enum {
   TRELLIS_OK = 0,
@@ -116,15 +122,44 @@ size_t trellis_workspace_bytes(int op, const trellis_linear *L, int batch_or_M, 
 /* Small-batch product y = had(had(x*su) @ W_hat) * sv.
  * ("Escha-W2 runs on Metal", reconstruction paragraph.)
  * L  : HOST pointer to the layer descriptor (its array pointers are device pointers).
- * x  : fp16 [B][in], y: fp16 out [B][out]; 1 <= B <= 8.
- * ws : zero-initialised device workspace of >= trellis_workspace_bytes(GEMV, L, B, 0) bytes. */
+ * x  : fp16 [B][in], y: fp16 out [B][out]; 1 <= B <= 8.  y must not overlap x.
+ * ws : zero-filled device workspace of >= trellis_workspace_bytes(GEMV, L, B, 0) bytes.
+ * One launch (the one-item case of trellis_gemv_list). */
 int trellis_gemv(const trellis_linear *L, const uint16_t *x, int B, uint16_t *y,
                  void *ws, size_t ws_bytes, void *stream);
 
+/* Several small-batch products in ONE launch: for each item p,
+ *   y_p = had(had(x_p*su_p) @ W_hat_p) * sv_p           (the trellis_gemv definition)
+ * Layers may differ in shape, K and codebook; the work of all of them is shared evenly by
+ * every compute unit, and each output column block is finished by the last workgroup to
+ * complete its share of it, so the whole list costs one launch.  Independent layers that
+ * run back to back (a model's q/k/v projections, gate and up, or layers whose inputs are
+ * ready together) take one call.
+ * ("Escha-W2 runs on Metal", reconstruction paragraph, per layer.)
+ * items : HOST array of n descriptors, 1 <= n <= TRELLIS_GEMV_LIST_MAX; each item's layer is
+ *         checked as for trellis_gemv, x_p fp16 [B][in_p], y_p fp16 out [B][out_p].  No
+ *         output may overlap another output or any input.
+ * B     : 1..8 rows, the same for every item.
+ * ws    : zero-filled device workspace of >= trellis_gemv_list_workspace_bytes(items, n, B)
+ *         bytes (see the conventions above).
+ * Returns TRELLIS_EUNSUPPORTED when the items have more than 16384 output column blocks
+ * (128 columns each) together. */
+#define TRELLIS_GEMV_LIST_MAX 8
+typedef struct {
+  trellis_linear L;
+  const uint16_t *x;
+  uint16_t *y;
+} trellis_gemv_item;
+
+/* Workspace bytes trellis_gemv_list needs (0 if the arguments are invalid or unsupported). */
+size_t trellis_gemv_list_workspace_bytes(const trellis_gemv_item *items, int n, int B);
+
+int trellis_gemv_list(const trellis_gemv_item *items, int n, int B, void *ws, size_t ws_bytes, void *stream);
+
 /* Prefill product, same definition as trellis_gemv for M rows (M >= 1).
  * x: fp16 [M][in], y: fp16 out [M][out].
- * ws: device workspace of >= trellis_workspace_bytes(GEMM, L, M, 0) bytes (holds the
- *     rotated activations). */
+ * ws: zero-filled device workspace of >= trellis_workspace_bytes(GEMM, L, M, 0) bytes
+ *     (holds the rotated activations after the reserved region).  Two launches. */
 int trellis_gemm(const trellis_linear *L, const uint16_t *x, int M, uint16_t *y,
                  void *ws, size_t ws_bytes, void *stream);
 
@@ -160,9 +195,9 @@ int trellis_gemm_fp8(const trellis_linear *L, const uint16_t *x, int M, uint16_t
  *               (shared_r, shared_s); 1: the output-side vectors are.  shared_r is fp16,
  *               shared_s is f32 or NULL.
  * y           : fp16 out [n][out].
- * An entry that is out of range or has an invalid K produces a zero output row and sets
- * the error word at the start of the workspace (uint32, non-zero = bad entry seen); check
- * tables once with trellis_validate_table(). */
+ * An entry that is out of range or has an invalid K produces a zero output row and sets bit
+ * 1 of the error word (see the conventions above); check tables once with
+ * trellis_validate_table().  One launch. */
 int trellis_moe_gemv(const trellis_linear *experts, int E, const int32_t *routed, int n,
                      int in_features, int out_features, const uint16_t *x, int x_per_expert,
                      const uint16_t *shared_r, const float *shared_s, int shared_side,
@@ -193,11 +228,11 @@ size_t trellis_moe_mlp_workspace_bytes(int hidden, int inter, int halves, int n)
  *           r_hidden_out/s_hidden_out: the shared down output vectors (s may be NULL).
  * act     : optional fp16 out [n][inter] receiving a_k (NULL: kept in the workspace).
  * y       : fp16 out [hidden]; n = 0 writes zeros.
- * ws      : zero-initialised device workspace of >= trellis_moe_mlp_workspace_bytes()
- *           bytes, 256-byte aligned; its first word is the error word.
- * Two partial/finishing launch pairs are enqueued.  A routed id out of range or an entry
- * with an invalid K contributes zero and sets the error word.  a_k is stored as fp16 and is
- * the input of down_e. */
+ * ws      : zero-filled device workspace of >= trellis_moe_mlp_workspace_bytes() bytes
+ *           (see the conventions above).
+ * Two launches (gate/up with the activation, then down with the weighted sum).  A routed id
+ * out of range or an entry with an invalid K contributes zero and sets bit 1 of the error
+ * word.  a_k is stored as fp16 and is the input of down_e. */
 int trellis_moe_mlp(const trellis_linear *gate_up, const trellis_linear *down, int E, int halves,
                     const int32_t *routed, const float *router_w, int n, int hidden, int inter,
                     const uint16_t *x, const uint16_t *r_hidden_in, const float *s_hidden_in,

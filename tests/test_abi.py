@@ -8,7 +8,8 @@ import pytest
 
 from trellis_coded_bit_amd import binding as tb
 
-EINVAL, EALIGN, EWORKSPACE = -1, -2, -3
+EINVAL, EALIGN, EWORKSPACE, EUNSUPPORTED = -1, -2, -3, -4
+RESERVED = 256 + 65536  # the reserved region at the start of every workspace
 
 
 @pytest.fixture(scope="module")
@@ -32,9 +33,26 @@ def test_exports_every_declared_symbol(L):
     assert set(names) >= {"trellis_decode_tiles", "had128_scale", "trellis_gemv", "trellis_gemm",
                           "trellis_moe_gemv", "trellis_workspace_bytes", "trellis_validate_table",
                           "trellis_last_error", "trellis_abi_version"}
-    for n in names:
-        assert hasattr(L, n), n
-    assert L.trellis_abi_version() == 1
+    inc = os.path.dirname(tb.HEADER)
+    headers = sorted(f for f in os.listdir(inc) if f.endswith(".h"))
+    assert "trellis_micro.h" in headers
+    for h in headers:
+        declared = tb.header_functions(os.path.join(inc, h))
+        assert declared, h
+        for n in declared:
+            assert hasattr(L, n), (h, n)
+    assert L.trellis_abi_version() == 2
+
+
+def test_micro_validation(L):
+    """The microbenchmarks reject bad sizes and kinds before launching (fake pointers)."""
+    assert L.trellis_micro_stream_read(0x10000, 8, 0, 0x20000, None) == EINVAL       # < 16 bytes
+    assert L.trellis_micro_stream_read(0x10008, 64, 0, 0x20000, None) == EALIGN     # misaligned
+    assert L.trellis_micro_stream_read(None, 64, 0, 0x20000, None) == EINVAL
+    assert L.trellis_micro_valu(1, 0, 1, 0x10000, 0x20000, 0x30000, None) == EINVAL  # iters < 1
+    assert L.trellis_micro_valu(1, 10, 9, 0x10000, 0x20000, 0x30000, None) == EINVAL  # waves/SIMD > 8
+    assert L.trellis_micro_mfma(0, 10, 5, 0x10000, 0x20000, 0x30000, None) == EINVAL  # waves/SIMD > 4
+    assert L.trellis_micro_mfma(0, 10, 1, 0x10004, 0x20000, 0x30000, None) == EALIGN
 
 
 def test_workspace_bytes(L):
@@ -69,6 +87,59 @@ def test_gemv_workspace_checks(L):
     assert L.trellis_gemv(ctypes.byref(c), 0x60000, 1, 0x70000, None, need, None) == EWORKSPACE
     assert L.trellis_gemv(ctypes.byref(c), 0x60000, 1, 0x70000, 0x80010, need, None) == EWORKSPACE
     assert L.trellis_gemv(ctypes.byref(c), None, 1, 0x70000, 0x80000, need, None) == EINVAL
+
+
+def test_every_workspace_starts_with_the_reserved_region(L):
+    """Every entry point's workspace is at least the reserved region (error word + the
+    small-batch counters) plus its own scratch, which lies after that region."""
+    c = lin()
+    for op, n in ((0, 1), (1, 64), (2, 8), (3, 64)):
+        cc = lin(cb=2) if op == 3 else c
+        assert L.trellis_workspace_bytes(op, ctypes.byref(cc), n if op != 2 else 1, 8) > RESERVED
+    assert L.trellis_workspace_bytes(1, ctypes.byref(c), 64, 0) >= RESERVED + 64 * 512 * 2
+
+
+def _items(*specs):
+    """(layer kwargs, x address, y address) -> a ctypes array of trellis_gemv_item."""
+    arr = (tb.CGemvItem * len(specs))()
+    for i, (kw, x, y) in enumerate(specs):
+        arr[i].L = lin(**kw)
+        arr[i].x = x
+        arr[i].y = y
+    return arr
+
+
+def test_gemv_list_validation(L):
+    ok = _items((dict(), 0x100000, 0x200000), (dict(K=3, in_features=1024, out_features=384), 0x300000, 0x400000))
+    need = L.trellis_gemv_list_workspace_bytes(ok, 2, 2)
+    assert need > RESERVED
+    # the list needs at least as much as each of its items alone
+    assert need >= L.trellis_workspace_bytes(0, ctypes.byref(lin()), 2, 0) - RESERVED
+    call = lambda items, n, B, nb=need, ws=0x8000000: L.trellis_gemv_list(items, n, B, ws, nb, None)
+    assert call(ok, 0, 1) == EINVAL
+    assert call(ok, 9, 1) == EINVAL
+    assert call(ok, 2, 0) == EINVAL and call(ok, 2, 9) == EINVAL
+    assert call(None, 1, 1) == EINVAL
+    assert call(ok, 2, 2, need - 1) == EWORKSPACE
+    assert call(ok, 2, 2, need, 0x8000010) == EWORKSPACE       # workspace not 256-byte aligned
+    bad = _items((dict(), 0x100000, 0x200000), (dict(K=5), 0x300000, 0x400000))
+    assert call(bad, 2, 1) == EINVAL and b"item 1" in L.trellis_last_error()
+    assert L.trellis_gemv_list_workspace_bytes(bad, 2, 1) == 0
+    # outputs may not overlap each other, nor any input
+    y_y = _items((dict(), 0x100000, 0x200000), (dict(), 0x300000, 0x200100))
+    assert call(y_y, 2, 1) == EINVAL and b"overlap" in L.trellis_last_error()
+    y_x = _items((dict(), 0x100000, 0x200000), (dict(), 0x2000F0, 0x400000))
+    assert call(y_x, 2, 1) == EINVAL and b"overlaps" in L.trellis_last_error()
+    own = _items((dict(), 0x100000, 0x1001F0),)  # y inside its own x
+    assert call(own, 1, 1) == EINVAL
+    nul = _items((dict(), None, 0x200000),)
+    assert call(nul, 1, 1) == EINVAL
+    mis = _items((dict(), 0x100001, 0x200000),)
+    assert call(mis, 1, 1) == EALIGN
+    # more output column blocks than the counter region holds: valid, but not supported
+    wide = _items((dict(in_features=128, out_features=128 * 16385), 0x100000, 0x10000000),)
+    assert L.trellis_gemv_list_workspace_bytes(wide, 1, 1) == 0
+    assert call(wide, 1, 1, 1 << 40) == EUNSUPPORTED
 
 
 def test_gemm_validation(L):
@@ -130,7 +201,7 @@ def test_moe_mlp_workspace_bytes(L):
     f = L.trellis_moe_mlp_workspace_bytes
     assert f(6144, 2048, 16, 8) > 8 * 2048 * 2
     assert f(6144, 2048, 1, 8) > 8 * 2048 * 2
-    assert f(6144, 2048, 16, 0) == 256
+    assert f(6144, 2048, 16, 0) == RESERVED
     assert f(100, 2048, 16, 8) == 0          # hidden not a multiple of 128
     assert f(6144, 2048, 3, 8) == 0          # inter not a multiple of 128 * halves
     assert f(6144, 2048, 0, 8) == 0

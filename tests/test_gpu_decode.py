@@ -44,26 +44,6 @@ def test_decode_single_k2_workload():
     assert np.array_equal(as_u16(w), O.decode_tiles(lin.code, 2).view(np.uint16))
 
 
-@pytest.mark.parametrize("which", ["gate", "up", "down"])
-def test_decode_full_size_sampled(which):
-    """Full dense-MLP shapes: decode on the GPU, compare sampled tile rows and columns."""
-    log_case(f"decode full-size {which}")
-    lin = synth.dense_mlp(0).layers[which]
-    K = lin.K
-    w, _ = tb.trellis_decode_tiles(to_dev(lin.code), K)
-    torch.cuda.synchronize()
-    Ti, Tj, _ = lin.code.shape
-    rng = np.random.default_rng(1)
-    rows = sorted({0, Ti - 1, *rng.integers(0, Ti, 2).tolist()})
-    cols = sorted({0, Tj - 1, *rng.integers(0, Tj, 2).tolist()})
-    for i in rows:
-        ref = O.decode_tiles(lin.code[i:i + 1], K)
-        assert np.array_equal(as_u16(w[16 * i:16 * i + 16]), ref.view(np.uint16)), (which, i)
-    for j in cols:
-        ref = O.decode_tiles(lin.code[:, j:j + 1], K)
-        assert np.array_equal(as_u16(w[:, 16 * j:16 * j + 16]), ref.view(np.uint16)), (which, j)
-
-
 def test_decode_deterministic():
     lin = synth.make_linear(np.random.SeedSequence(77), 3, 256, 256)
     c = to_dev(lin.code)

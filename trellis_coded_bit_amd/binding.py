@@ -91,15 +91,27 @@ def lib() -> ctypes.CDLL:
             L.trellis_moe_mlp.restype = i32
             L.trellis_moe_mlp.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                           sz, vp]
+            L.trellis_micro_cus.restype = i32
+            L.trellis_micro_cus.argtypes = []
+            L.trellis_micro_stream_read.restype = i32
+            L.trellis_micro_stream_read.argtypes = [vp, sz, i32, vp, vp]
+            L.trellis_micro_valu.restype = i32
+            L.trellis_micro_valu.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+            L.trellis_micro_mfma.restype = i32
+            L.trellis_micro_mfma.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+            L.trellis_gemv_list_workspace_bytes.restype = sz
+            L.trellis_gemv_list_workspace_bytes.argtypes = [vp, i32, i32]
+            L.trellis_gemv_list.restype = i32
+            L.trellis_gemv_list.argtypes = [vp, i32, i32, vp, sz, vp]
             L.trellis_validate_table.restype = i32
             L.trellis_validate_table.argtypes = [ctypes.POINTER(CLinear), i32, i32, i32, i32]
             _lib = L
     return _lib
 
 
-def header_functions() -> List[str]:
-    """Names of the functions include/trellis.h declares."""
-    txt = open(HEADER).read()
+def header_functions(header: str = HEADER) -> List[str]:
+    """Names of the functions a header under include/ declares (default include/trellis.h)."""
+    txt = open(header).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const\s+char\s*\*)\s*\*?\s*(\w+)\s*\(", txt, flags=re.M)
 
@@ -134,18 +146,42 @@ def _req(t: torch.Tensor, dtype: torch.dtype, name: str, device=None) -> None:
 # Workspaces: zero-filled once, reused by back-to-back calls on one stream.
 # ---------------------------------------------------------------------------------------
 
-_ws: Dict[Tuple[int, int, int], torch.Tensor] = {}
+_ws: Dict[Tuple[int, int], torch.Tensor] = {}
 
 
-def workspace(nbytes: int, device: torch.device, op: int) -> torch.Tensor:
-    """Per (device, stream, op kind): the GEMM workspace holds activations, the GEMV/MoE
-    workspaces hold self-resetting counters, so the kinds never share one."""
-    key = (device.index if device.index is not None else torch.cuda.current_device(), _stream(), op)
+def workspace(nbytes: int, device: torch.device, op: int = 0) -> torch.Tensor:
+    """One zero-filled workspace per (device, stream), grown on demand.  Every entry point
+    leaves the reserved region at the start of a workspace as it found it, so all of them
+    share one buffer (``op`` is accepted for compatibility and ignored)."""
+    key = (device.index if device.index is not None else torch.cuda.current_device(), _stream())
     w = _ws.get(key)
     if w is None or w.numel() < nbytes:
         w = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws[key] = w
     return w
+
+
+def _out(out: Optional[torch.Tensor], shape, device, dtype=torch.float16, name="out") -> torch.Tensor:
+    """A new output tensor, or the caller's after checking dtype, device, contiguity and size
+    (the kernels write exactly prod(shape) elements through its pointer)."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _req(out, dtype, name, device)
+    n = 1
+    for d in shape:
+        n *= int(d)
+    if out.numel() != n:
+        raise ValueError(f"{name} has {out.numel()} elements, expected {n} (shape {tuple(shape)})")
+    return out
+
+
+def _ws_arg(ws: Optional[torch.Tensor], nb: int, device) -> torch.Tensor:
+    if ws is None:
+        return workspace(nb, device)
+    _req(ws, torch.uint8, "ws", device)
+    if ws.numel() < nb:
+        raise ValueError(f"workspace of {ws.numel()} bytes < {nb}")
+    return ws
 
 
 class TrellisLinear:
@@ -220,10 +256,9 @@ def had128_scale(x: torch.Tensor, r: Optional[torch.Tensor] = None, s: Optional[
         _req(r, torch.float16, "r", x.device)
     if s is not None:
         _req(s, torch.float32, "s", x.device)
-    if out is None:
-        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
-    else:
-        _req(out, out.dtype, "out", x.device)
+    if out is not None and out.dtype not in (torch.float16, torch.float32):
+        raise TypeError("out must be float16 or float32")
+    out = _out(out, tuple(x.shape), x.device, out.dtype if out is not None else (out_dtype or x.dtype))
     _check(lib().had128_scale(x.data_ptr(), int(x.dtype == torch.float32), rows, n, _ptr(r), _ptr(s), int(post),
                               out.data_ptr(), int(out.dtype == torch.float32), _stream()))
     return out
@@ -234,32 +269,91 @@ def trellis_gemv(layer: TrellisLinear, x: torch.Tensor, out: Optional[torch.Tens
     """x fp16 [B, in] (B = 1..8) -> y fp16 [B, out].  ``ws``: optional uint8 workspace tensor
     (at least ``layer.workspace_bytes(TRELLIS_OP_GEMV, B)`` bytes), e.g. for graph capture."""
     _req(x, torch.float16, "x", layer.code.device)
+    if x.numel() % layer.in_features:
+        raise ValueError(f"x has {x.numel()} elements, not a multiple of in_features={layer.in_features}")
     x2 = x.reshape(-1, layer.in_features)
     B = x2.shape[0]
-    if out is None:
-        out = torch.empty((B, layer.out_features), dtype=torch.float16, device=x.device)
-    nb = layer.workspace_bytes(TRELLIS_OP_GEMV, B)
-    if ws is None:
-        ws = workspace(nb, x.device, TRELLIS_OP_GEMV)
-    elif ws.numel() < nb:
-        raise ValueError(f"workspace of {ws.numel()} bytes < {nb}")
+    out = _out(out, (B, layer.out_features), x.device)
+    ws = _ws_arg(ws, layer.workspace_bytes(TRELLIS_OP_GEMV, B), x.device)
     _check(lib().trellis_gemv(ctypes.byref(layer.c()), x2.data_ptr(), B, out.data_ptr(), ws.data_ptr(), ws.numel(),
                               _stream()))
     return out
+
+
+class CGemvItem(ctypes.Structure):
+    """Mirror of ``trellis_gemv_item`` in include/trellis.h."""
+
+    _fields_ = [("L", CLinear), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+GEMV_LIST_MAX = 8
+
+
+def _gemv_items(layers: Sequence[TrellisLinear], xs: Sequence[torch.Tensor], outs: Sequence[torch.Tensor]):
+    items = (CGemvItem * len(layers))()
+    for i, (l, x, y) in enumerate(zip(layers, xs, outs)):
+        items[i].L = l.c()
+        items[i].x = x.data_ptr()
+        items[i].y = y.data_ptr()
+    return items
+
+
+def trellis_gemv_list_workspace_bytes(layers: Sequence[TrellisLinear], B: int) -> int:
+    """Workspace bytes of trellis_gemv_list for these layers at batch B (fake x/y pointers:
+    only shapes matter)."""
+    items = (CGemvItem * len(layers))()
+    for i, l in enumerate(layers):
+        items[i].L = l.c()
+        items[i].x = 0x1000 * (2 * i + 1) << 32
+        items[i].y = 0x1000 * (2 * i + 2) << 32
+    nb = lib().trellis_gemv_list_workspace_bytes(items, len(layers), B)
+    if nb == 0:
+        raise TrellisError(-4, lib().trellis_last_error().decode() or "unsupported list")
+    return nb
+
+
+def trellis_gemv_list(layers: Sequence[TrellisLinear], xs: Sequence[torch.Tensor],
+                      outs: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                      ws: Optional[torch.Tensor] = None) -> List[torch.Tensor]:
+    """One launch for several small-batch products: xs[p] fp16 [B, in_p] -> fp16 [B, out_p],
+    the same B (1..8) for every layer."""
+    n = len(layers)
+    if n < 1 or n > GEMV_LIST_MAX or len(xs) != n:
+        raise ValueError(f"1..{GEMV_LIST_MAX} layers with one input each expected")
+    dev = layers[0].code.device
+    x2s, B = [], None
+    for l, x in zip(layers, xs):
+        _req(x, torch.float16, "x", dev)
+        if x.numel() % l.in_features:
+            raise ValueError(f"x has {x.numel()} elements, not a multiple of in_features={l.in_features}")
+        x2 = x.reshape(-1, l.in_features)
+        if B is None:
+            B = x2.shape[0]
+        elif x2.shape[0] != B:
+            raise ValueError("every input must have the same batch B")
+        x2s.append(x2)
+    outs = list(outs) if outs is not None else [None] * n
+    if len(outs) != n:
+        raise ValueError("one output (or None) per layer expected")
+    ys = [_out(o, (B, l.out_features), dev) for o, l in zip(outs, layers)]
+    items = _gemv_items(layers, x2s, ys)
+    nb = lib().trellis_gemv_list_workspace_bytes(items, n, B)
+    if nb == 0:
+        _check(lib().trellis_gemv_list(items, n, B, None, 0, _stream()))
+    ws = _ws_arg(ws, nb, dev)
+    _check(lib().trellis_gemv_list(items, n, B, ws.data_ptr(), ws.numel(), _stream()))
+    return ys
 
 
 def trellis_gemm(layer: TrellisLinear, x: torch.Tensor, out: Optional[torch.Tensor] = None,
                  ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """x fp16 [M, in] -> y fp16 [M, out]."""
     _req(x, torch.float16, "x", layer.code.device)
+    if x.dim() != 2 or x.shape[1] != layer.in_features:
+        raise ValueError(f"x must be [M, {layer.in_features}]")
     M = x.shape[0]
-    if out is None:
-        out = torch.empty((M, layer.out_features), dtype=torch.float16, device=x.device)
-    nb = layer.workspace_bytes(TRELLIS_OP_GEMM, M)
-    if ws is None:
-        ws = workspace(nb, x.device, TRELLIS_OP_GEMM)
-    elif ws.numel() < nb:
-        raise ValueError(f"workspace of {ws.numel()} bytes < {nb}")
+    out = _out(out, (M, layer.out_features), x.device)
+    ws = _ws_arg(ws, layer.workspace_bytes(TRELLIS_OP_GEMM, M), x.device)
     _check(lib().trellis_gemm(ctypes.byref(layer.c()), x.data_ptr(), M, out.data_ptr(), ws.data_ptr(), ws.numel(),
                               _stream()))
     return out
@@ -280,14 +374,11 @@ def trellis_gemm_fp8(layer: TrellisLinear, x: torch.Tensor, out: Optional[torch.
                      ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """x fp16 [M, in] -> y fp16 [M, out] on the FP8 matrix cores (layer.cb must be 2)."""
     _req(x, torch.float16, "x", layer.code.device)
+    if x.dim() != 2 or x.shape[1] != layer.in_features:
+        raise ValueError(f"x must be [M, {layer.in_features}]")
     M = x.shape[0]
-    if out is None:
-        out = torch.empty((M, layer.out_features), dtype=torch.float16, device=x.device)
-    nb = layer.workspace_bytes(TRELLIS_OP_GEMM_FP8, M)
-    if ws is None:
-        ws = workspace(nb, x.device, TRELLIS_OP_GEMM_FP8)
-    elif ws.numel() < nb:
-        raise ValueError(f"workspace of {ws.numel()} bytes < {nb}")
+    out = _out(out, (M, layer.out_features), x.device)
+    ws = _ws_arg(ws, layer.workspace_bytes(TRELLIS_OP_GEMM_FP8, M), x.device)
     _check(lib().trellis_gemm_fp8(ctypes.byref(layer.c()), x.data_ptr(), M, out.data_ptr(), ws.data_ptr(),
                                   ws.numel(), _stream()))
     return out
@@ -349,24 +440,38 @@ def trellis_moe_gemv(table: ExpertTable, routed: torch.Tensor, x: torch.Tensor, 
     dev = routed.device
     _req(x, torch.float16, "x", dev)
     n = routed.numel()
-    if out is None:
-        out = torch.empty((n, table.out_features), dtype=torch.float16, device=dev)
-    nb = table.workspace_bytes(n)
-    if ws is None:
-        ws = workspace(nb, dev, TRELLIS_OP_MOE_GEMV)
-    elif ws.numel() < nb:
-        raise ValueError(f"workspace of {ws.numel()} bytes < {nb}")
+    if x.numel() != (n if x_per_expert else 1) * table.in_features:
+        raise ValueError(f"x must have {'n*' if x_per_expert else ''}in = "
+                         f"{(n if x_per_expert else 1) * table.in_features} elements")
+    for name, v, dt in (("shared_r", shared_r, torch.float16), ("shared_s", shared_s, torch.float32)):
+        if v is not None:
+            _req(v, dt, name, dev)
+            side_n = table.in_features if shared_side == 0 else table.out_features
+            if v.numel() != side_n:
+                raise ValueError(f"{name} must have {side_n} elements")
+    out = _out(out, (n, table.out_features), dev)
+    ws = _ws_arg(ws, table.workspace_bytes(n), dev)
     _check(lib().trellis_moe_gemv(table.table.data_ptr(), table.E, routed.data_ptr(), n, table.in_features,
                                   table.out_features, x.data_ptr(), int(x_per_expert), _ptr(shared_r),
                                   _ptr(shared_s), shared_side, out.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
     return out
 
 
-def moe_error_word(device="cuda") -> int:
-    """The error word of the current stream's workspace (non-zero: a bad table entry was seen)."""
-    key = (torch.device(device).index or 0, _stream(), TRELLIS_OP_MOE_GEMV)
-    w = _ws.get(key)
-    return 0 if w is None else int(w[:4].view(torch.int32).item())
+def error_word(ws: Optional[torch.Tensor] = None, device="cuda") -> int:
+    """The error word of a workspace (default: the current stream's shared one); it is
+    sticky (bit 1: a bad routed id or table entry was skipped; bit 2: a bounded wait ran
+    out).  Synchronises."""
+    if ws is None:
+        ws = _ws.get((torch.device(device).index or 0, _stream()))
+    return 0 if ws is None else int(ws[:4].view(torch.int32).item())
+
+
+def clear_error_word(ws: Optional[torch.Tensor] = None, device="cuda") -> None:
+    """Clear a workspace's error word (a fill on the current stream; graph-safe)."""
+    if ws is None:
+        ws = _ws.get((torch.device(device).index or 0, _stream()))
+    if ws is not None:
+        ws[:4].zero_()
 
 
 class MoEMLPTables:
@@ -435,22 +540,68 @@ def trellis_moe_mlp(tables: MoEMLPTables, routed: torch.Tensor, router_w: torch.
             _req(v, dt, name, dev)
             if v.numel() != tables.hidden:
                 raise ValueError(f"{name} must have {tables.hidden} elements")
-    if out is None:
-        out = torch.empty(tables.hidden, dtype=torch.float16, device=dev)
-    else:
-        _req(out, torch.float16, "out", dev)
+    out = _out(out, (tables.hidden,), dev)
     if act is not None:
         _req(act, torch.float16, "act", dev)
         if act.numel() != n * tables.inter:
             raise ValueError(f"act must have n*inter = {n * tables.inter} elements")
-    nb = tables.workspace_bytes(n)
-    if ws is None:
-        ws = workspace(nb, dev, TRELLIS_OP_MOE_MLP)
-    elif ws.numel() < nb:
-        raise ValueError(f"workspace of {ws.numel()} bytes < {nb}")
+    ws = _ws_arg(ws, tables.workspace_bytes(n), dev)
     _check(lib().trellis_moe_mlp(tables.gate_up.table.data_ptr(), tables.down.table.data_ptr(), tables.E,
                                  tables.halves, routed.data_ptr(), router_w.data_ptr(), n, tables.hidden,
                                  tables.inter, x.data_ptr(), _ptr(r_hidden_in), _ptr(s_hidden_in),
                                  _ptr(r_hidden_out), _ptr(s_hidden_out), _ptr(act), out.data_ptr(),
                                  ws.data_ptr(), ws.numel(), _stream()))
     return out
+
+
+# ---------------------------------------------------------------------------------------
+# Microbenchmarks (include/trellis_micro.h): the machine's ceilings, not the method
+# ---------------------------------------------------------------------------------------
+
+MICRO_VALU = {"v_add_u32": 0, "v_mul_lo_u32": 1, "v_mul_u32_u24": 2, "v_mad_u32_u24": 3, "v_mad_u32_u16": 4,
+              "v_mul_lo_u16_sdwa": 5, "v_pk_mul_lo_u16": 6, "v_bfe_u32": 7, "v_alignbit_b32": 8,
+              "v_perm_b32": 9, "v_bitop3_b32": 10, "v_lshrrev_b32": 11, "v_add_f16_sdwa": 12,
+              "v_mul_u32_u24_sdwa": 13, "v_fma_f32": 14}
+MICRO_DECODE = {"decode_tile": 100, "decode_tile_mfma": 101, "decode_tile_u24": 102}
+MICRO_MFMA = {"f16_16x16x32": (0, 16 * 16 * 32), "f16_32x32x16": (1, 32 * 32 * 16),
+              "f8_16x16x128": (2, 16 * 16 * 128), "f8_32x32x64": (3, 32 * 32 * 64)}
+
+
+def micro_cus() -> int:
+    return int(lib().trellis_micro_cus())
+
+
+def micro_stream_read(buf: torch.Tensor, blocks: int = 0) -> torch.Tensor:
+    """Enqueue one stream read of ``buf`` (any dtype, 16-byte aligned, size a multiple of 16)."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    nb = buf.numel() * buf.element_size()
+    grid = blocks if blocks > 0 else 8 * micro_cus()
+    sink = torch.empty(grid * 256, dtype=torch.int32, device=buf.device)
+    _check(lib().trellis_micro_stream_read(buf.data_ptr(), nb, blocks, sink.data_ptr(), _stream()))
+    return sink
+
+
+def micro_clock_kernel(kind: str, name: str, iters: int, waves_per_simd: int, device="cuda"):
+    """Run one VALU / decode / MFMA micro kernel; returns (cycles, ticks, ms): int64 tensors
+    with one entry per workgroup, and the launch's wall time from events (synchronises)."""
+    nblk = micro_cus() * waves_per_simd
+    cycles = torch.zeros(nblk, dtype=torch.int64, device=device)
+    ticks = torch.zeros(nblk, dtype=torch.int64, device=device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if kind == "mfma":
+        sink = torch.empty(nblk * 256, dtype=torch.float32, device=device)
+        e0.record()
+        st = lib().trellis_micro_mfma(MICRO_MFMA[name][0], iters, waves_per_simd, cycles.data_ptr(),
+                                      ticks.data_ptr(), sink.data_ptr(), _stream())
+    else:
+        op = MICRO_VALU.get(name, MICRO_DECODE.get(name))
+        sink = torch.empty(nblk * 256, dtype=torch.int32, device=device)
+        e0.record()
+        st = lib().trellis_micro_valu(op, iters, waves_per_simd, cycles.data_ptr(), ticks.data_ptr(),
+                                      sink.data_ptr(), _stream())
+    e1.record()
+    if st < 0:
+        _check(st)
+    torch.cuda.synchronize()
+    return cycles, ticks, e0.elapsed_time(e1)

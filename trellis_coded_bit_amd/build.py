@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtrellis.so")
-SOURCES = ["api.cpp", "decode.hip", "hadamard.hip", "gemv.hip", "gemm.hip", "encode.hip"]
+SOURCES = ["api.cpp", "decode.hip", "hadamard.hip", "gemv.hip", "gemm.hip", "encode.hip", "micro.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = [

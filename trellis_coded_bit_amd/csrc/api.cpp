@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "../../include/trellis.h"
+#include "../../include/trellis_micro.h"
 #include "launch.h"
 
 namespace {
@@ -101,9 +102,14 @@ size_t trellis_workspace_bytes(int op, const trellis_linear *L, int batch_or_M, 
       L->out_features % 128)
     return 0;
   switch (op) {
-    case TRELLIS_OP_GEMV:
+    case TRELLIS_OP_GEMV: {
       if (batch_or_M < 1 || batch_or_M > 8) return 0;
-      return trellis::gemv_workspace_bytes(1, L->in_features, L->out_features, batch_or_M);
+      trellis::GemvLaunch a{};
+      a.n_list = 1;
+      a.list[0].L = *L;
+      a.B = batch_or_M;
+      return trellis::gemv_workspace_bytes(a);
+    }
     case TRELLIS_OP_GEMM:
       if (batch_or_M < 0) return 0;
       return trellis::gemm_workspace_bytes(L->in_features, L->out_features, batch_or_M);
@@ -123,29 +129,83 @@ int trellis_gemv(const trellis_linear *L, const uint16_t *x, int B, uint16_t *y,
   g_err[0] = 0;
   int st = check_linear(L, 1);
   if (st) return st;
+  trellis_gemv_item it;
+  it.L = *L;
+  it.x = x;
+  it.y = y;
+  return trellis_gemv_list(&it, 1, B, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks a list of small-batch problems and fills the launch description.
+int make_list_launch(const trellis_gemv_item *items, int n, int B, trellis::GemvLaunch *a) {
+  if (!items) return fail(TRELLIS_EINVAL, "items is NULL");
+  if (n < 1 || n > TRELLIS_GEMV_LIST_MAX) return fail(TRELLIS_EINVAL, "n=%d not in 1..%d", n, TRELLIS_GEMV_LIST_MAX);
   if (B < 1 || B > 8) return fail(TRELLIS_EINVAL, "B=%d not in 1..8", B);
-  if (!x || !y) return fail(TRELLIS_EINVAL, "x or y is NULL");
-  if (!aligned(x, 2) || !aligned(y, 2)) return fail(TRELLIS_EALIGN, "x/y must be 2-byte aligned");
-  if (L->out_features / 128 > trellis::gemv_max_column_blocks())
-    return fail(TRELLIS_EINVAL, "out=%d exceeds %d column blocks", L->out_features, trellis::gemv_max_column_blocks());
-  const size_t need = trellis::gemv_workspace_bytes(1, L->in_features, L->out_features, B);
+  *a = trellis::GemvLaunch{};
+  for (int p = 0; p < n; ++p) {
+    const trellis_gemv_item &it = items[p];
+    int st = check_linear(&it.L, 1);
+    if (st) {
+      char tmp[512];
+      snprintf(tmp, sizeof(tmp), "item %d: %s", p, g_err);
+      snprintf(g_err, sizeof(g_err), "%s", tmp);
+      return st;
+    }
+    if (!it.x || !it.y) return fail(TRELLIS_EINVAL, "item %d: x or y is NULL", p);
+    if (!aligned(it.x, 2) || !aligned(it.y, 2)) return fail(TRELLIS_EALIGN, "item %d: x/y must be 2-byte aligned", p);
+    a->list[p].L = it.L;
+    a->list[p].x = it.x;
+    a->list[p].y = it.y;
+  }
+  // outputs must not overlap each other or any input (every output is written once, after
+  // every input of the launch may still be read)
+  for (int p = 0; p < n; ++p) {
+    const char *y0 = reinterpret_cast<const char *>(items[p].y);
+    const char *y1 = y0 + (size_t)B * items[p].L.out_features * 2;
+    for (int q = 0; q < n; ++q) {
+      const char *x0 = reinterpret_cast<const char *>(items[q].x);
+      const char *x1 = x0 + (size_t)B * items[q].L.in_features * 2;
+      if (y0 < x1 && x0 < y1) return fail(TRELLIS_EINVAL, "item %d's output overlaps item %d's input", p, q);
+      if (q != p) {
+        const char *z0 = reinterpret_cast<const char *>(items[q].y);
+        const char *z1 = z0 + (size_t)B * items[q].L.out_features * 2;
+        if (y0 < z1 && z0 < y1) return fail(TRELLIS_EINVAL, "outputs of items %d and %d overlap", p, q);
+      }
+    }
+  }
+  a->n_list = n;
+  a->table = nullptr;
+  a->B = B;
+  a->shared_side = -1;
+  a->finish = trellis::kFinishPlain;
+  return TRELLIS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t trellis_gemv_list_workspace_bytes(const trellis_gemv_item *items, int n, int B) {
+  trellis::GemvLaunch a;
+  if (make_list_launch(items, n, B, &a) != TRELLIS_OK) return 0;
+  return trellis::gemv_workspace_bytes(a);
+}
+
+int trellis_gemv_list(const trellis_gemv_item *items, int n, int B, void *ws, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  trellis::GemvLaunch a;
+  int st = make_list_launch(items, n, B, &a);
+  if (st) return st;
+  const size_t need = trellis::gemv_workspace_bytes(a);
+  if (need == 0)
+    return fail(TRELLIS_EUNSUPPORTED, "more than %d output column blocks or 2^31 units in one call",
+                trellis::kMaxFinishGroups);
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(TRELLIS_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
-  trellis::GemvLaunch a{};
-  a.single = *L;
-  a.table = nullptr;
-  a.E = 0;
-  a.routed = nullptr;
-  a.n_problems = 1;
-  a.in_features = L->in_features;
-  a.out_features = L->out_features;
-  a.B = B;
-  a.x = x;
-  a.x_per_problem = 0;
-  a.y = y;
-  a.shared_r = nullptr;
-  a.shared_s = nullptr;
-  a.shared_side = -1;
   return hip_status(trellis::launch_gemv(a, ws, ws_bytes, as_stream(stream)), "trellis_gemv launch");
 }
 
@@ -211,16 +271,15 @@ int trellis_moe_gemv(const trellis_linear *experts, int E, const int32_t *routed
   if (shared_side >= 0 && !shared_r) return fail(TRELLIS_EINVAL, "shared_r is NULL");
   if (x_per_expert != 0 && x_per_expert != 1) return fail(TRELLIS_EINVAL, "x_per_expert must be 0 or 1");
   if (n == 0) return TRELLIS_OK;
-  if ((long long)n * (out_features / 128) > trellis::gemv_max_column_blocks())
-    return fail(TRELLIS_EINVAL, "n*out/128 exceeds %d column blocks", trellis::gemv_max_column_blocks());
   if (!routed || !x || !y) return fail(TRELLIS_EINVAL, "routed, x or y is NULL");
   if (!aligned(experts, 8) || !aligned(routed, 4) || !aligned(x, 2) || !aligned(y, 2))
     return fail(TRELLIS_EALIGN, "misaligned table, routed, x or y");
   const size_t need = trellis::gemv_workspace_bytes(n, in_features, out_features, 1);
+  if (need == 0)
+    return fail(TRELLIS_EUNSUPPORTED, "n*out/128 exceeds %d column blocks", trellis::kMaxFinishGroups);
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(TRELLIS_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
   trellis::GemvLaunch a{};
-  memset(&a.single, 0, sizeof(a.single));
   a.table = experts;
   a.E = E;
   a.group = 1;
@@ -266,6 +325,8 @@ int trellis_moe_mlp(const trellis_linear *gate_up, const trellis_linear *down, i
       !aligned(r_hidden_out, 2) || !aligned(s_hidden_in, 4) || !aligned(s_hidden_out, 4))
     return fail(TRELLIS_EALIGN, "misaligned table, vector or buffer");
   const size_t need = trellis::moe_mlp_workspace_bytes(hidden, inter, halves, n);
+  if (need == 0)
+    return fail(TRELLIS_EUNSUPPORTED, "n*inter/128 exceeds %d column blocks", 2 * trellis::kMaxFinishGroups);
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(TRELLIS_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
   trellis::MlpLaunch m{};
@@ -332,6 +393,50 @@ int trellis_validate_table(const trellis_linear *host_table, int E, int in_featu
                   L.out_features, in_features, out_features);
   }
   return TRELLIS_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// Microbenchmarks (include/trellis_micro.h)
+// ---------------------------------------------------------------------------------------
+
+int trellis_micro_cus(void) { return trellis::micro_cus(); }
+
+int trellis_micro_stream_read(const void *buf, size_t bytes, int blocks, uint32_t *sink, void *stream) {
+  g_err[0] = 0;
+  if (!buf || !sink) return fail(TRELLIS_EINVAL, "buf or sink is NULL");
+  if (bytes < 16 || bytes % 16) return fail(TRELLIS_EINVAL, "bytes=%zu must be a positive multiple of 16", bytes);
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(TRELLIS_EALIGN, "buf must be 16-byte aligned");
+  if (blocks < 0 || blocks > (1 << 20)) return fail(TRELLIS_EINVAL, "blocks=%d out of range", blocks);
+  return hip_status(trellis::launch_micro_stream_read(buf, bytes, blocks, sink, as_stream(stream)),
+                    "trellis_micro_stream_read launch");
+}
+
+int trellis_micro_valu(int op, int iters, int waves_per_simd, uint64_t *cycles, uint64_t *ticks, uint32_t *sink,
+                       void *stream) {
+  g_err[0] = 0;
+  if (iters < 1 || waves_per_simd < 1 || waves_per_simd > 8)
+    return fail(TRELLIS_EINVAL, "iters=%d >= 1 and waves_per_simd=%d in 1..8 expected", iters, waves_per_simd);
+  if (!cycles || !ticks || !sink) return fail(TRELLIS_EINVAL, "cycles, ticks or sink is NULL");
+  if (!aligned(cycles, 8) || !aligned(ticks, 8) || !aligned(sink, 4)) return fail(TRELLIS_EALIGN, "misaligned output");
+  int blocks = 0;
+  const hipError_t e = trellis::launch_micro_valu(op, iters, waves_per_simd, cycles, ticks, sink, as_stream(stream), &blocks);
+  if (e == hipErrorInvalidValue) return fail(TRELLIS_EINVAL, "unknown micro kernel %d", op);
+  const int st = hip_status(e, "trellis_micro_valu launch");
+  return st ? st : blocks;
+}
+
+int trellis_micro_mfma(int kind, int iters, int waves_per_simd, uint64_t *cycles, uint64_t *ticks, float *sink,
+                       void *stream) {
+  g_err[0] = 0;
+  if (iters < 1 || waves_per_simd < 1 || waves_per_simd > 4)
+    return fail(TRELLIS_EINVAL, "iters=%d >= 1 and waves_per_simd=%d in 1..4 expected", iters, waves_per_simd);
+  if (!cycles || !ticks || !sink) return fail(TRELLIS_EINVAL, "cycles, ticks or sink is NULL");
+  if (!aligned(cycles, 8) || !aligned(ticks, 8) || !aligned(sink, 4)) return fail(TRELLIS_EALIGN, "misaligned output");
+  int blocks = 0;
+  const hipError_t e = trellis::launch_micro_mfma(kind, iters, waves_per_simd, cycles, ticks, sink, as_stream(stream), &blocks);
+  if (e == hipErrorInvalidValue) return fail(TRELLIS_EINVAL, "unknown matrix kernel %d", kind);
+  const int st = hip_status(e, "trellis_micro_mfma launch");
+  return st ? st : blocks;
 }
 
 }  // extern "C"

@@ -3,7 +3,8 @@
 // ("Escha-W2 runs on Metal", reconstruction paragraph; decode as in decode.hip.)
 //
 // Two launches:
-//   1. rotate: XH = H128(X*su) (unnormalised butterfly) as fp16 in the workspace, stored in
+//   1. rotate: XH = H128(X*su) (unnormalised butterfly, times an exact 2^-4) as fp16 in the
+//      workspace (after its reserved region), stored in
 //      1 KB blocks of 16 rows x one k-step laid out exactly as the MFMA A operands are held
 //      by the lanes, so every A-operand load is one contiguous, fully used 1 KB piece.  It
 //      also clears the split-tile counters.
@@ -29,7 +30,9 @@
 //      weights.
 //
 //      A range covering a whole tile finishes it: output Hadamard across the tile's 128
-//      columns (16 lanes x 8 registers per row), scales, the exact 1/128, fp16 stores.
+//      columns (16 lanes x 8 registers per row), scales, the exact 2^-3 left of the two
+//      1/sqrt(128) (2^-7 for the FP8 product, whose row scales undo the quantisation), fp16
+//      stores.
 //      A tile split between two ranges: the first contributor to arrive stores its fp32
 //      partial tile; the second adds it to its registers and finishes the tile.  Tiles
 //      split among three or more (short ranges): every contributor stores, the last to
@@ -62,6 +65,7 @@ struct GemmParams {
   uint16_t *y;
   float *partials;     // [2G][kTileFloats]
   uint32_t *counters;  // [T][2] (arrived, stored) per tile, zeroed by the rotation launch
+  uint32_t *errword;   // the workspace's error word
   int M, in, out;
   int S;               // k-step pairs per tile (the unit of the ranges)
   int nNT;             // column tiles
@@ -174,7 +178,9 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t *__restrict_
   uint16_t *dst = stage + (i >> 2) * 512 + q * 8 + 2 * (i & 3);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const half2_t pr = {(_Float16)v[2 * g], (_Float16)v[2 * g + 1]};
+    // stored times 2^-4 (exact): close to the normalised 2^-3.5, so a block whose normalised
+    // rotation fits fp16 does not overflow here
+    const half2_t pr = {(_Float16)(v[2 * g] * 0.0625f), (_Float16)(v[2 * g + 1] * 0.0625f)};
     *reinterpret_cast<half2_t *>(dst + 16 * 8 * g) = pr;
   }
   __syncthreads();
@@ -225,11 +231,6 @@ typedef floatx4 Acc[4][8];
 
 // Output Hadamard, scales and stores for tile (mt, nt).  Lane holds rows
 // 64*wave + 16*mb + 4*(lane >> 4) + r and columns 16*nb + (lane & 15).
-// Raw buffer resource over `bytes` bytes at `base` (loads past the end return zero).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, long long bytes) {
-  const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
-}
 
 // Staging through LDS uses the wave's own 1 KB of B ring slot 0 (idle between pieces).
 // F8: the rows carry the activations' dequantisation scales (rowscale), applied with sv.
@@ -249,7 +250,9 @@ __device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int m
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
     const int col = nt * kNT + 16 * nb + n16;
-    float s = h2f(P.rout[col]) * (1.0f / 128.0f);
+    // fp16 product: the activations were stored times 2^-4, so 2^-7 / 2^-4 remains; FP8:
+    // the row scales restore the unnormalised activations, 2^-7 remains
+    float s = h2f(P.rout[col]) * (F8 ? (1.0f / 128.0f) : (1.0f / 8.0f));
     if (P.s_out) s *= P.s_out[col];
     sv[nb] = s;
   }
@@ -319,7 +322,6 @@ __device__ __forceinline__ void finish_tile(const GemmParams &P, Acc &acc, int m
 // (coalesced 1 KB per instruction).  They are written and read with device-scope
 // coherence (the sc1 cache policy: through the per-XCD L2s), because the workgroup that
 // adds them may run on another XCD.
-constexpr int kSC1 = 16;  // cache-policy operand of the buffer intrinsics: SC1
 
 __device__ __forceinline__ void store_partial(const GemmParams &P, int slot, const Acc &acc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -788,12 +790,19 @@ __device__ __forceinline__ void gemm_ranges(const GemmParams &P, Ring ring, CRin
           signal = t;
         } else {
           if (threadIdx.x == 0) {
-            for (int spin = 0; spin < (1 << 24); ++spin) {
-              if (__hip_atomic_load(P.counters + 2 * t + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
-              __builtin_amdgcn_s_sleep(2);
+            // Bounded: the other contributor has arrived (it is running) and publishes its
+            // partial within one piece.  If the wait ever ran out, the sum would miss that
+            // partial; the error word says so.
+            bool seen = false;
+            for (int spin = 0; spin < (1 << 24) && !seen; ++spin) {
+              seen = __hip_atomic_load(P.counters + 2 * t + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+              if (!seen) __builtin_amdgcn_s_sleep(2);
             }
+            if (!seen) __hip_atomic_fetch_or(P.errword, kErrWaitExpired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
           __syncthreads();
+          // the partial is read after its publication was seen, with device-scope (sc1) loads,
+          // which read the coherent copy: no cache invalidation is needed
           const int c = g0 + g1 - g;  // the other contributor
           add_partial(P, 2 * c + (range_start(P, c) >= ts ? 0 : 1), acc, false);
           finish = true;
@@ -803,11 +812,14 @@ __device__ __forceinline__ void gemm_ranges(const GemmParams &P, Ring ring, CRin
         // partial tile; the last to arrive adds all of them in range order, so the sum
         // does not depend on which one arrives last.
         store_partial(P, own, acc);
-        __syncthreads();  // every thread's partial stores have completed
+        // Every thread waits for its own partial stores before the barrier (the barrier
+        // alone does not wait for global stores), so the arrival below publishes them.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
         if (threadIdx.x == 0)
           arrivals = __hip_atomic_fetch_add(P.counters + 2 * t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
-        if (arrivals == (uint32_t)(g1 - g0)) {
+        if (arrivals == (uint32_t)(g1 - g0)) {  // (the others' partials: sc1 loads after their arrivals)
           // A contributor's piece of tile t is the start piece of its range (slot 2c) when
           // its range starts inside t, else the end piece (slot 2c + 1).
           for (int c = g0; c <= g1; ++c)
@@ -819,7 +831,9 @@ __device__ __forceinline__ void gemm_ranges(const GemmParams &P, Ring ring, CRin
     if (finish) finish_tile<F8>(P, acc, t / P.nNT, t % P.nNT, reinterpret_cast<u32x4 *>(ring));
   }
   if (signal >= 0) {
-    __syncthreads();  // the stores of the last piece's partial have completed
+    // every thread's stores of the last piece's partial have completed, then the barrier
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
     if (threadIdx.x == 0)
       __hip_atomic_fetch_add(P.counters + 2 * signal + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -855,7 +869,7 @@ struct Plan {
   int S, nNT, T, G;
   long long I;
   int q, r;
-  size_t xh_bytes, pmax_off, rowscale_off, partials_off, counters_off, bytes;
+  size_t xh_bytes, xh_off, pmax_off, rowscale_off, partials_off, counters_off, bytes;
 };
 
 // f8: iterations are single 128-row k-steps and the activations are E4M3 bytes, with the
@@ -881,7 +895,8 @@ Plan plan(int in_features, int out_features, int M, bool f8 = false) {
   p.r = (int)(p.I % G);
   const size_t Mpad = (size_t)((M + 15) / 16) * 16;  // whole 16-row blocks
   p.xh_bytes = Mpad * in_features * (f8 ? 1 : 2);
-  p.pmax_off = p.xh_bytes;
+  p.xh_off = kWsReserved;  // (the reserved region of every workspace is left alone)
+  p.pmax_off = p.xh_off + (p.xh_bytes + 255) / 256 * 256;
   p.rowscale_off = p.pmax_off + (f8 ? (Mpad * (in_features / 128) * 4 + 255) / 256 * 256 : 0);
   p.partials_off = p.rowscale_off + (f8 ? (Mpad * 4 + 255) / 256 * 256 : 0);
   p.counters_off = p.partials_off + (size_t)2 * p.G * kTileFloats * sizeof(float);
@@ -892,12 +907,12 @@ Plan plan(int in_features, int out_features, int M, bool f8 = false) {
 }  // namespace
 
 size_t gemm_workspace_bytes(int in_features, int out_features, int M) {
-  if (M <= 0) return 256;
+  if (M <= 0) return kWsReserved;
   return plan(in_features, out_features, M).bytes;
 }
 
 size_t gemm_fp8_workspace_bytes(int in_features, int out_features, int M) {
-  if (M <= 0) return 256;
+  if (M <= 0) return kWsReserved;
   return plan(in_features, out_features, M, true).bytes;
 }
 
@@ -910,7 +925,7 @@ hipError_t launch_gemm_fp8(const trellis_linear &L, const uint16_t *x, int M, ui
   if (p.I >= (1LL << 31)) return hipErrorInvalidValue;  // 32-bit iteration arithmetic
   if ((long long)(M + 15) / 16 * (L.in_features / 128) >= (1LL << 31)) return hipErrorInvalidValue;
   char *w = static_cast<char *>(ws);
-  uint8_t *xq = reinterpret_cast<uint8_t *>(w);
+  uint8_t *xq = reinterpret_cast<uint8_t *>(w + p.xh_off);
   float *pmax = reinterpret_cast<float *>(w + p.pmax_off);
   float *rowscale = reinterpret_cast<float *>(w + p.rowscale_off);
   uint32_t *counters = reinterpret_cast<uint32_t *>(w + p.counters_off);
@@ -933,6 +948,7 @@ hipError_t launch_gemm_fp8(const trellis_linear &L, const uint16_t *x, int M, ui
   P.y = y;
   P.partials = reinterpret_cast<float *>(w + p.partials_off);
   P.counters = counters;
+  P.errword = reinterpret_cast<uint32_t *>(w);
   P.M = M;
   P.in = L.in_features;
   P.out = L.out_features;
@@ -957,7 +973,7 @@ hipError_t launch_gemm(const trellis_linear &L, const uint16_t *x, int M, uint16
   if (ws_bytes < p.bytes) return hipErrorInvalidValue;
   if (p.G > (1 << 20)) return hipErrorInvalidValue;
   if (p.I >= (1LL << 31)) return hipErrorInvalidValue;  // 32-bit iteration arithmetic
-  uint16_t *xh = static_cast<uint16_t *>(ws);
+  uint16_t *xh = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + p.xh_off);
   uint32_t *counters = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + p.counters_off);
   if ((long long)(M + 15) / 16 * (L.in_features / 128) >= (1LL << 31)) return hipErrorInvalidValue;
   const unsigned rgrid = (unsigned)((M + 15) / 16 * (L.in_features / 128));
@@ -977,6 +993,7 @@ hipError_t launch_gemm(const trellis_linear &L, const uint16_t *x, int M, uint16
   P.y = y;
   P.partials = reinterpret_cast<float *>(static_cast<char *>(ws) + p.partials_off);
   P.counters = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + p.counters_off);
+  P.errword = static_cast<uint32_t *>(ws);
   P.M = M;
   P.in = L.in_features;
   P.out = L.out_features;

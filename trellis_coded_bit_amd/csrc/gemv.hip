@@ -1,38 +1,50 @@
-// trellis_gemv / trellis_moe_gemv: fused small-batch products against trellis-coded weights.
+// trellis_gemv / trellis_gemv_list / trellis_moe_gemv / trellis_moe_mlp: fused small-batch
+// products against trellis-coded weights.
 //
 // y = had(had(x*su) @ W_hat) * sv  ("Escha-W2 runs on Metal", reconstruction paragraph),
-// for B = 1..8 rows, over a list of problems (one layer, or the routed entries of an expert
-// pointer table -- "EXLR8" page: per-expert widths, a pointer table re-read every launch,
-// one hidden-side rotation shared by all experts).
+// for B = 1..8 rows, over a list of problems: up to eight layers of any shapes with their
+// own inputs and outputs, or the routed entries of an expert pointer table ("EXLR8" page:
+// per-expert widths, a pointer table re-read every launch, one hidden-side rotation shared
+// by all experts).
 //
-// Two launches.
+// One launch per problem list.  A "unit" is one 128-row input block I times one 128-column
+// output block J of one problem, i.e. 8x8 tiles; units are numbered problem by problem,
+// column block by column block, I fastest.  They are cut into "chunks" of consecutive
+// units: G equal big chunks first, one per workgroup (every one resident at once), then a
+// tail of small chunks.  A workgroup runs its big chunk, then takes small chunks from a
+// queue (one device-scope atomic each) until none is left, so the compute units that start
+// late (the XCDs are dispatched one after another) or run slow take fewer of them.  Inside a workgroup
+// (4 waves) every wave takes two of the unit's eight tile rows:
+//   * loads: the wave's 2 x 8 tiles are 2 x 256K contiguous bytes, copied straight from
+//     global memory into a wave-private LDS ring (global_load_lds, 16 B per lane, fully
+//     coalesced) several units ahead of use; a lane's circular window is read as two LDS
+//     words of its tile;
+//   * input rotation: per sub-range the workgroup butterflies x*su (unnormalised) and
+//     stores fp16 MFMA A-operands in LDS, each value twice and scaled by an exact 2^-4
+//     (below);
+//   * contraction: per tile each lane decodes its four symbols (trellis_device.h) to four
+//     MCG hash words and feeds them UNSUMMED to v_mfma_f32_16x16x32_f16 as eight fp16
+//     B-elements along k.  The A operand repeats each activation for the lo and hi halves,
+//     so the matrix core forms x*lo + x*hi in fp32 and the codebook's lo+hi addition costs
+//     no vector instruction.  One MFMA covers one tile; batch rows ride in the 16 M rows
+//     (rows past B read a duplicate activation and are ignored).  This fp32 sum of the
+//     halves is the exact value before the format's fp16 rounding; it differs from the
+//     rounded codebook value by at most half an fp16 ulp.
+// Finishing, in the same launch: a chunk's fp32 partial y_pre[B][128] of each column block
+// it touches (its "segments") is stored with device-scope (sc1) stores.  At the end of the
+// chunk, once every thread has waited for those stores to complete, the workgroup counts the
+// chunk in per column block with one device-scope atomic.  Whoever brings a block's count to
+// the number of chunks that cover it adds the block's partials in chunk order (so the sum
+// does not depend on who arrives last), applies the output Hadamard, the scales and the
+// exact factor that remains of the two 1/sqrt(128), and writes fp16 y; then it resets the
+// block's counter for the next call.  Blocks finish as soon as their last chunk is done,
+// while other chunks are still decoding.
 //
-// 1. gemv_partial_kernel (stream-K over "units").  A unit is one 128-row input block I
-//    times one 128-column output block J of one problem p, i.e. 8x8 tiles; units are
-//    numbered u = (p*nJ + J)*nI + I and the G workgroups take equal contiguous ranges of u,
-//    so every workgroup streams the same number of code bytes whatever the matrix shape.
-//    Each workgroup writes one fp32 partial sum y_pre[B][128] per column block it touches
-//    (its "segment") into the workspace.  Inside a workgroup (4 waves) every wave takes
-//    two of the unit's eight tile rows:
-//      * loads: the wave's 2 x 8 tiles are 2 x 256K contiguous bytes, copied straight
-//        from global memory into a wave-private LDS ring (global_load_lds, 16 B per lane,
-//        fully coalesced) several units ahead of use; a lane's circular window is read as
-//        two LDS words of its tile;
-//      * balance: the workgroups resident on one CU set their issue priority from the
-//        share of their range still to do, so they finish together;
-//      * input rotation: per sub-range the workgroup butterflies x*su (unnormalised) and
-//        stores fp16 MFMA A-operands in LDS, each value twice (below);
-//      * contraction: per tile each lane decodes its four symbols (trellis_device.h) to
-//        four MCG hash words and feeds them UNSUMMED to v_mfma_f32_16x16x32_f16 as eight
-//        fp16 B-elements along k.  The A operand repeats each activation for the lo and hi
-//        halves, so the matrix core forms x*lo + x*hi in fp32 and the codebook's lo+hi
-//        addition costs no VALU work.  One MFMA covers one tile; batch rows ride in the
-//        16 M rows (rows past B read a duplicate activation and are ignored).  This fp32
-//        sum of the halves is the exact value before the format's fp16 rounding; it
-//        differs from the rounded codebook value by at most half an fp16 ulp.
-// 2. gemv_finish_kernel: one workgroup per column block adds its partials in workgroup
-//    order (deterministic), applies the output Hadamard, the scales and the exact 1/128
-//    that replaces the two 1/sqrt(128) factors, and writes fp16 y.
+// Magnitudes: the butterfly of a 128-block grows values by up to 128 (sqrt(128) for random
+// signs).  The rotated activations are stored as fp16 times 2^-4, close to the normalised
+// 1/sqrt(128) = 2^-3.5, so any block whose normalised rotation is representable in fp16 is
+// (2^-4 is exact; the output side applies 2^-7 / 2^-4 = 2^-3).
+#include <climits>
 #include <cstdlib>
 #include <type_traits>
 
@@ -52,22 +64,35 @@ constexpr int kABudget = 32768;  // LDS bytes for A operands
 // workgroups (16 waves) share a CU; more waves per SIMD hide the decode's latencies better
 // than deeper rings hide memory latency (measured).
 constexpr int kRingBytes = 7168;
+constexpr float kInScale = 0.0625f;  // 2^-4 on the stored rotated activations
+constexpr float kOutScale = 0.125f;  // 2^-7 / 2^-4: the rest of the two 1/sqrt(128)
 
 struct GemvParams {
-  GemvLaunch L;
+  // (the fields read before a workgroup's first code copy come first)
+  int U;                // total units
+  int CH;               // units per big chunk (chunks 0 .. G-1)
+  int CHs;              // units per small chunk (the tail, chunks G ..)
+  int big_units;        // units in the big chunks: min(U, G * CH)
+  int n_chunks;
+  int G;                // workgroups
+  int kA;               // units per sub-range (A-operand capacity)
+  int maxseg;           // column blocks a chunk can touch
+  int nI, nJ;           // table mode: the uniform shape in blocks
+  int ubase[kMaxList + 1];  // list mode: first unit of each problem (U past the last)
+  int qbase[kMaxList + 1];  // list mode: first column block of each problem
   uint32_t *errword;
-  float *partials;
-  int U;   // total units
-  int G;   // workgroups of the partial kernel
-  int nI, nJ, maxseg;
-  int kA;  // units per sub-range (A-operand capacity)
+  uint32_t *queue;      // [2]: chunks handed out past the first G; workgroups done
+  uint32_t *counters;   // [finish groups], zero between calls
+  float *partials;      // [n_chunks][maxseg][B][128]
+  long long partial_bytes;
+  GemvLaunch L;
 };
 
 // Dynamic LDS layout for batch B.
 struct Lds {
-  uint32_t *a;      // [kA][8 tile rows][4 groups][B][4 words]
+  uint32_t *a;      // [kA][8 tile rows][4 groups][B][4 words]; at the end: arrival flags
   uint32_t *tiles;  // [kWaves][kRingBytes / 4]: each wave's code ring
-  float *red;       // [kWaves][B][128]
+  float *red;       // [kWaves][B][128]; at the end: one block's sums
 };
 
 __host__ __device__ constexpr size_t lds_a_bytes(int B, int kA) { return (size_t)kA * 8 * 4 * B * 16; }
@@ -84,53 +109,171 @@ __device__ __forceinline__ Lds lds_carve(char *base, int B, int kA) {
   return s;
 }
 
+// One problem, resolved (wave-uniform).
 struct Problem {
   const uint32_t *code;
   const uint16_t *rin, *rout;
   const float *s_in, *s_out;
+  const uint16_t *x;
+  uint16_t *y;
   int K;
   int cb;  // 1: MCG fp16 values; 2: the same rounded to E4M3
+  int in, out;
   bool ok;
 };
 
-// TABLE = false: the launch is known to be a single layer (no table lookups at all).
-template <bool TABLE = true>
+template <bool LIST>
 __device__ __forceinline__ Problem get_problem(const GemvParams &P, int p) {
-  trellis_linear d = P.L.single;
-  bool ok = true;
-  if (TABLE && P.L.table) {
+  Problem r;
+  const int B = P.L.B;
+  if constexpr (LIST) {
+    const GemvItem &it = P.L.list[p];
+    r.code = reinterpret_cast<const uint32_t *>(it.L.code);
+    r.rin = it.L.rin;
+    r.rout = it.L.rout;
+    r.s_in = it.L.s_in;
+    r.s_out = it.L.s_out;
+    r.K = it.L.K;
+    r.cb = it.L.cb;
+    r.in = it.L.in_features;
+    r.out = it.L.out_features;
+    r.x = it.x;
+    r.y = it.y;
+    r.ok = r.K >= 2 && r.K <= 4 && (r.cb == 1 || r.cb == 2);
+  } else {
     const int grp = P.L.group;
     const int slot = grp == 1 ? p : p / grp;
     const int e = P.L.routed[slot];
-    if (e < 0 || e >= P.L.E) ok = false;
-    else d = P.L.table[e * grp + (p - slot * grp)];
+    bool ok = e >= 0 && e < P.L.E;
+    trellis_linear d{};
+    if (ok) d = P.L.table[e * grp + (p - slot * grp)];
+    r.code = reinterpret_cast<const uint32_t *>(d.code);
+    r.K = d.K;
+    r.cb = d.cb;
+    r.rin = d.rin;
+    r.s_in = d.s_in;
+    r.rout = d.rout;
+    r.s_out = d.s_out;
+    if (P.L.shared_side == 0) { r.rin = P.L.shared_r; r.s_in = P.L.shared_s; }
+    if (P.L.shared_side == 1) { r.rout = P.L.shared_r; r.s_out = P.L.shared_s; }
+    r.in = P.L.in_features;
+    r.out = P.L.out_features;
+    r.x = P.L.x + (P.L.x_per_problem ? (size_t)p * B * r.in : (size_t)0);
+    r.y = P.L.y + (size_t)p * B * r.out;
+    r.ok = ok && d.K >= 2 && d.K <= 4 && (d.cb == 1 || d.cb == 2) && d.code != nullptr && r.rin != nullptr &&
+           r.rout != nullptr && d.in_features == P.L.in_features && d.out_features == P.L.out_features;
   }
-  Problem r;
-  r.code = reinterpret_cast<const uint32_t *>(d.code);
-  r.K = d.K;
-  r.cb = d.cb;
-  r.rin = d.rin;
-  r.s_in = d.s_in;
-  r.rout = d.rout;
-  r.s_out = d.s_out;
-  if (P.L.shared_side == 0) { r.rin = P.L.shared_r; r.s_in = P.L.shared_s; }
-  if (P.L.shared_side == 1) { r.rout = P.L.shared_r; r.s_out = P.L.shared_s; }
-  if (ok) {
-    ok = d.K >= 2 && d.K <= 4 && (d.cb == 1 || d.cb == 2) && d.code != nullptr && r.rin != nullptr &&
-         r.rout != nullptr && d.in_features == P.L.in_features &&
-         d.out_features == P.L.out_features;
-  }
-  r.ok = ok;
   return r;
 }
 
-// First unit of workgroup g, and the workgroup owning unit u (largest g with start(g) <= u).
-// 32-bit arithmetic: the launch checks G * U < 2^32.
-__host__ __device__ __forceinline__ int wg_start(int g, int U, int G) {
-  return (int)(((unsigned)g * (unsigned)U) / (unsigned)G);
+
+// Unit and column-block numbering over the problems.
+template <bool LIST>
+__device__ __forceinline__ int problem_of_unit(const GemvParams &P, int u) {
+  if constexpr (LIST) {
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxList; ++i) p += u >= P.ubase[i];  // (entries past the list hold U)
+    return p;
+  } else {
+    return u / (P.nI * P.nJ);
+  }
 }
-__host__ __device__ __forceinline__ int owner(int u, int U, int G) {
-  return (int)(((unsigned)(u + 1) * (unsigned)G - 1u) / (unsigned)U);
+template <bool LIST>
+__device__ __forceinline__ int problem_of_block(const GemvParams &P, int q) {
+  if constexpr (LIST) {
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxList; ++i) p += q >= P.qbase[i];
+    return p;
+  } else {
+    return q / P.nJ;
+  }
+}
+template <bool LIST>
+__device__ __forceinline__ int units_base(const GemvParams &P, int p) {
+  if constexpr (LIST) return P.ubase[p];
+  else return p * P.nI * P.nJ;
+}
+template <bool LIST>
+__device__ __forceinline__ int blocks_base(const GemvParams &P, int p) {
+  if constexpr (LIST) return P.qbase[p];
+  else return p * P.nJ;
+}
+template <bool LIST>
+__device__ __forceinline__ int nI_of(const GemvParams &P, int p) {
+  if constexpr (LIST) return P.L.list[p].L.in_features / 128;
+  else return P.nI;
+}
+template <bool LIST>
+__device__ __forceinline__ int block_of_unit(const GemvParams &P, int u) {
+  const int p = problem_of_unit<LIST>(P, u);
+  return blocks_base<LIST>(P, p) + (u - units_base<LIST>(P, p)) / nI_of<LIST>(P, p);
+}
+// The chunks that meet column block q: c_lo .. c_hi.  Every chunk after c_lo starts inside
+// block q, so q is its first segment; q is segment seg_lo of chunk c_lo.
+struct BlockChunks {
+  int lo, hi, seg_lo;
+};
+__device__ __forceinline__ int chunk_start(const GemvParams &P, int c) {
+  return c < P.G ? c * P.CH : P.big_units + (c - P.G) * P.CHs;
+}
+__device__ __forceinline__ int chunk_end(const GemvParams &P, int c) {
+  return c < P.G ? min(P.big_units, (c + 1) * P.CH) : min(P.U, P.big_units + (c + 1 - P.G) * P.CHs);
+}
+__device__ __forceinline__ int chunk_of(const GemvParams &P, int u) {
+  return u < P.big_units ? u / P.CH : P.G + (u - P.big_units) / P.CHs;
+}
+template <bool LIST>
+__device__ __forceinline__ BlockChunks block_chunks(const GemvParams &P, int q) {
+  const int p = problem_of_block<LIST>(P, q);
+  const int nI = nI_of<LIST>(P, p);
+  const int qs = units_base<LIST>(P, p) + (q - blocks_base<LIST>(P, p)) * nI;
+  BlockChunks c;
+  c.lo = chunk_of(P, qs);
+  c.hi = chunk_of(P, qs + nI - 1);
+  c.seg_lo = q - block_of_unit<LIST>(P, chunk_start(P, c.lo));
+  return c;
+}
+
+// Finish groups: the column blocks whose partials one finishing workgroup combines.
+//   plain: one block;  SwiGLU: the gate and the up block of one (slot, half, J);
+//   weighted: block J of every problem.
+template <bool LIST>
+__device__ __forceinline__ int group_of_block(const GemvParams &P, int q) {
+  if (LIST || P.L.finish == kFinishPlain) return q;
+  const int p = q / P.nJ, J = q - p * P.nJ;
+  if (P.L.finish == kFinishSwiGLU) {
+    const int H = P.L.halves;
+    const int slot = p / (2 * H), h = (p - slot * 2 * H) % H;
+    return (slot * H + h) * P.nJ + J;
+  }
+  return J;
+}
+template <bool LIST>
+__device__ __forceinline__ int group_arrivals(const GemvParams &P, int f) {
+  auto n = [&](int q) {
+    const BlockChunks c = block_chunks<LIST>(P, q);
+    return c.hi - c.lo + 1;
+  };
+  if (LIST || P.L.finish == kFinishPlain) return n(f);
+  if (P.L.finish == kFinishSwiGLU) {
+    const int H = P.L.halves, nJ = P.nJ;
+    const int slot = f / (H * nJ), rem = f - slot * H * nJ;
+    const int pg = slot * 2 * H + rem / nJ, J = rem - (rem / nJ) * nJ;
+    return n(pg * nJ + J) + n((pg + H) * nJ + J);
+  }
+  int t = 0;
+  for (int k = 0; k < P.L.n_problems; ++k) t += n(k * P.nJ + f);
+  return t;
+}
+
+// Wave issue priority (s_setprio takes an immediate).
+__device__ __forceinline__ void set_priority(int prio) {
+  if (prio >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (prio == 2) __builtin_amdgcn_s_setprio(2);
+  else if (prio == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
 }
 
 // Orders this wave's LDS accesses (all lanes of one wave run in lockstep and the LDS
@@ -141,13 +284,6 @@ __device__ __forceinline__ void wave_sync() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Wave issue priority (s_setprio takes an immediate).
-__device__ __forceinline__ void set_priority(int prio) {
-  if (prio >= 3) __builtin_amdgcn_s_setprio(3);
-  else if (prio == 2) __builtin_amdgcn_s_setprio(2);
-  else if (prio == 1) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(0);
-}
 
 // ---------------------------------------------------------------------------------------
 // Input rotation.  a[((s*8 + ti)*4 + g)*B + m] holds, for tile row ti of unit s and batch
@@ -174,9 +310,74 @@ __device__ __forceinline__ void rotation_compute(int B, int n, int wave, const R
       for (int h = 0; h < 2; ++h) {
         const int ti = (lane >> 4) + 4 * h, rr = lane & 15;
         const int g = (rr & 7) >> 1, w = 2 * (rr >> 3) + (rr & 1);
-        const uint32_t hv = f2h(h ? vb : va);
+        const uint32_t hv = f2h((h ? vb : va) * kInScale);
         sm.a[((((s * 8 + ti) * 4 + g) * B + b) << 2) + w] = hv | (hv << 16);
       }
+    }
+  }
+}
+
+// The same rotation with 16-byte accesses (x, rin and s_in 16-byte aligned): lanes
+// 16j..16j+15 of wave w take task w + kWaves*j (its unit's 128-block of one batch row), lane
+// i of the group holding elements 8i..8i+7 -- four load instructions per lane for a task
+// instead of six per task and wave.  Three butterfly stages run in registers and four
+// across the group's 16 lanes; element k = 8i + t lands where the scalar form puts it.
+struct RotVec {
+  u32x4 x, r;
+  floatx4 s0, s1;
+};
+
+template <bool WITH_S>
+__device__ __forceinline__ RotVec rot_vec_load(const uint16_t *xp, const uint16_t *rin, const float *s_in, int in,
+                                               int B, int task, int I) {
+  const int i = threadIdx.x & 15;
+  const int s = task / B, b = task - s * B;
+  (void)s;
+  const int k = I * 128 + 8 * i;
+  RotVec q;
+  q.x = ldg(reinterpret_cast<const u32x4 *>(xp + (size_t)b * in + k));
+  q.r = ldg(reinterpret_cast<const u32x4 *>(rin + k));
+  if constexpr (WITH_S) {
+    q.s0 = ldg(reinterpret_cast<const floatx4 *>(s_in + k));
+    q.s1 = ldg(reinterpret_cast<const floatx4 *>(s_in + k + 4));
+  } else {
+    q.s0 = floatx4{1.f, 1.f, 1.f, 1.f};
+    q.s1 = floatx4{1.f, 1.f, 1.f, 1.f};
+  }
+  return q;
+}
+
+__device__ __forceinline__ void rot_vec_compute(int B, int n, int task, const RotVec &q, const Lds &sm) {
+  const int lane = threadIdx.x & 63, i = lane & 15;
+  float v[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t xw = q.x[t >> 1], rw = q.r[t >> 1];
+    const float xs = h2f((t & 1) ? (uint16_t)(xw >> 16) : (uint16_t)xw);
+    const float rs = h2f((t & 1) ? (uint16_t)(rw >> 16) : (uint16_t)rw);
+    v[t] = xs * rs * (t < 4 ? q.s0[t] : q.s1[t - 4]);
+  }
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if ((t & h) == 0) {
+        const float a = v[t], b = v[t + h];
+        v[t] = a + b;
+        v[t + h] = a - b;
+      }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) fwht_stage1(v[t], lane);
+  if (task < n * B) {
+    const int s = task / B, b = task - s * B;
+    // element k = 8i + t: tile row ti = i >> 1, in-tile row rr = 8(i & 1) + t, so group
+    // g = t >> 1 and word w = 2(i & 1) + (t & 1): one 8-byte write per pair of elements
+    const int ti = i >> 1;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t h0 = f2h(v[2 * g] * kInScale), h1 = f2h(v[2 * g + 1] * kInScale);
+      *reinterpret_cast<u32x2 *>(sm.a + ((((s * 8 + ti) * 4 + g) * B + b) << 2) + 2 * (i & 1)) =
+          u32x2{h0 | (h0 << 16), h1 | (h1 << 16)};
     }
   }
 }
@@ -192,9 +393,12 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// End of a segment (the workgroup's share of column block q): reduce the waves'
-// accumulators and store the partial (not waited for: code copies in flight keep streaming).
-__device__ __forceinline__ void publish_partial(const GemvParams &P, const Lds &sm, int q, floatx4 (&acc)[8]) {
+// End of a segment (chunk c's share of a column block, its segment seg): reduce the waves'
+// accumulators and store the partial with device-scope stores.  The stores are not waited
+// for here (code copies in flight keep streaming); the arrival at the end of the chunk
+// waits for them.
+__device__ __forceinline__ void publish_partial(const GemvParams &P, const Lds &sm, int c, int seg,
+                                                floatx4 (&acc)[8]) {
   const int B = P.L.B;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
@@ -208,14 +412,13 @@ __device__ __forceinline__ void publish_partial(const GemvParams &P, const Lds &
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
   lds_barrier();
-  const int g = blockIdx.x;
-  const int seg = q - wg_start(g, P.U, P.G) / P.nI;
-  float *part = P.partials + ((size_t)g * P.maxseg + seg) * kMaxB * 128;
+  const __amdgpu_buffer_rsrc_t rp = buffer_rsrc(P.partials, P.partial_bytes);
+  const uint32_t base = (uint32_t)(((size_t)c * P.maxseg + seg) * B * 128 * 4);
   for (int idx = tid; idx < B * 128; idx += kThreads) {
     float v = sm.red[idx];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) v += sm.red[w * B * 128 + idx];
-    part[idx] = v;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rp, base + 4 * idx, 0, kSC1);
   }
   lds_barrier();
 }
@@ -281,21 +484,23 @@ __device__ __forceinline__ void dma_unit(const uint32_t *row0, size_t row_stride
   }
 }
 
-// Units [ub, ue) of problem p (width K), in sub-ranges of at most P.kA units.  Each
-// sub-range issues its rotation loads and its first code copies, rotates while the code is
-// in flight, then streams with SLOTS - 1 units in flight per wave.
+// Units [ub, ue) of problem p (width K), part of chunk c, in sub-ranges of at most P.kA
+// units.  Each sub-range issues its rotation loads and its first code copies, rotates while
+// the code is in flight, then streams with SLOTS - 1 units in flight per wave.  q0: the
+// chunk's first column block (segment numbering).  fresh: the workgroup's first part (its
+// first code copy was issued before the set-up).
 // CB = 2 (the E4M3 codebook, "EXLR8" page): each lane's four values are the E4M3-rounded
 // codebook values, converted back to fp16 (exact) and fed to v_mfma_f32_16x16x16_f16 with
 // the A operand's duplicated words repacked once per tile row into (x0, x1), (x8, x9).
-template <int K, int CB = 1>
-__device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &pr, int p, int ub, int ue,
-                            bool fresh) {
+template <int K, int CB, bool LIST>
+__device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &pr, int p, int ub, int ue, int c,
+                            int q0, bool fresh) {
   using RG = Ring<K>;
   constexpr int NW = RG::NW;
   constexpr int SLOTS = RG::SLOTS;
   const int B = P.L.B;
-  const int Tj = P.L.out_features / 16;
-  const int nI = P.nI;
+  const int Tj = pr.out / 16;
+  const int nI = pr.in / 128;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, grp = lane >> 4;
@@ -306,14 +511,14 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
   const size_t row_stride = (size_t)Tj * NW;
   const uint32_t *code = pr.code + (size_t)(2 * wave) * row_stride;
   const size_t row_block_words = 8 * row_stride;
-  const int first = __builtin_amdgcn_readfirstlane(ub - p * P.nI * P.nJ);
+  const int first = __builtin_amdgcn_readfirstlane(ub - units_base<LIST>(P, p));
   const int total = __builtin_amdgcn_readfirstlane(ue - ub);
-  const int in = P.L.in_features;
-  const uint16_t *xp = P.L.x + (P.L.x_per_problem ? (size_t)p * B * in : (size_t)0);
+  const int in = pr.in;
+  const uint16_t *xp = pr.x;
+  const int qp = __builtin_amdgcn_readfirstlane(blocks_base<LIST>(P, p) - q0);  // segment of J = 0
 
-  // The workgroup's first copy goes out before the rest of the set-up (priority
-  // thresholds, sub-range bookkeeping, lane constants): its address needs only the first
-  // unit's (I, J).
+  // The workgroup's first copy goes out before the rest of the set-up (priority thresholds,
+  // sub-range bookkeeping, lane constants): its address needs only the first unit's (I, J).
   if (fresh) {
     const int I0 = __builtin_amdgcn_readfirstlane(first % nI), J0 = __builtin_amdgcn_readfirstlane(first / nI);
     dma_unit<K>(code + (size_t)I0 * row_block_words + (size_t)(8 * J0) * NW, row_stride, ring, true);
@@ -322,15 +527,15 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
   floatx4 acc[8];
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // Issue priority from the share of the workgroup's range still to do, in quarters (3 =
-  // more than three quarters left).  The waves of a CU otherwise issue oldest-first, so the
-  // workgroups resident on a CU would finish one after another and the last would run with
-  // few waves at the end; with this rule the ones behind catch up and they finish together.
-  // Priority p applies from unit t[p] = u1 - floor((p + 1) * units / 4) on.
-  const int wg_u1 = __builtin_amdgcn_readfirstlane(wg_start(blockIdx.x + 1, P.U, P.G));
-  const int wg_units = __builtin_amdgcn_readfirstlane(wg_u1 - wg_start(blockIdx.x, P.U, P.G));
-  const int t2 = wg_u1 - (3 * wg_units) / 4, t1 = wg_u1 - (2 * wg_units) / 4, t0 = wg_u1 - wg_units / 4;
-  auto prio_at = [&](int c) { return c >= t0 ? 0 : c >= t1 ? 1 : c >= t2 ? 2 : 3; };
+  // Issue priority from the share of the chunk still to do, in quarters (3 = more than three
+  // quarters left).  The waves of a CU otherwise issue oldest-first, so the workgroups
+  // resident on a CU would finish one after another and the last would run with few waves at
+  // the end; with this rule the ones behind catch up and they finish together.  Priority p
+  // applies from unit t[p] = u1 - floor((p + 1) * units / 4) on.
+  const int ch_u1 = __builtin_amdgcn_readfirstlane(chunk_end(P, c));
+  const int ch_units = __builtin_amdgcn_readfirstlane(ch_u1 - chunk_start(P, c));
+  const int t2 = ch_u1 - (3 * ch_units) / 4, t1 = ch_u1 - (2 * ch_units) / 4, t0 = ch_u1 - ch_units / 4;
+  auto prio_at = [&](int u) { return u >= t0 ? 0 : u >= t1 ? 1 : u >= t2 ? 2 : 3; };
 
   for (int sb = 0; sb < total; sb += P.kA) {
     const int n = __builtin_amdgcn_readfirstlane(min(P.kA, total - sb));
@@ -366,6 +571,15 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
     if (sb == 0) set_priority(prio_at(ub));  // (after the first copy is on its way)
     // Rotation loads: straight-line code (tasks past the last are clamped to it and their
     // values ignored), so all of them are in flight together.
+    const bool vec = ((reinterpret_cast<uintptr_t>(xp) | reinterpret_cast<uintptr_t>(pr.rin) |
+                       reinterpret_cast<uintptr_t>(pr.s_in)) & 15) == 0;
+    if (vec) {
+      const int task = min(wave + kWaves * (lane >> 4), n * B - 1);
+      const int I = (first + sb + task / B) % nI;
+      const RotVec q = pr.s_in ? rot_vec_load<true>(xp, pr.rin, pr.s_in, in, B, task, I)
+                               : rot_vec_load<false>(xp, pr.rin, pr.s_in, in, B, task, I);
+      rot_vec_compute(B, n, wave + kWaves * (lane >> 4), q, sm);
+    } else {
     RotLoads rq;
     auto load_tasks = [&](auto with_s) {
 #pragma unroll
@@ -390,6 +604,7 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
     if (pr.s_in) load_tasks(std::true_type{});
     else load_tasks(std::false_type{});
     rotation_compute(B, n, wave, rq, sm);
+    }
     __syncthreads();  // (also waits for unit 0)
 #pragma unroll
     for (int j = 1; j < SLOTS - 1; ++j) prime(j);
@@ -405,8 +620,8 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
       }
       wait_vmcnt<RG::WAIT>();  // unit k has landed
       {
-        const int c = ub + sb + k;
-        if (c == t2 || c == t1 || c == t0) set_priority(prio_at(c));
+        const int u = ub + sb + k;
+        if (u == t2 || u == t1 || u == t0) set_priority(prio_at(u));
       }
       const uint32_t *ub_ = ring + slot * (RG::UNIT_BYTES / 4);
 #pragma unroll
@@ -435,7 +650,7 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
         }
       }
       wave_sync();
-      if (cur_I == nI - 1 || sb + k == total - 1) publish_partial(P, sm, p * P.nJ + cur_J, acc);
+      if (cur_I == nI - 1 || sb + k == total - 1) publish_partial(P, sm, c, qp + cur_J, acc);
       if (++cur_I == nI) { cur_I = 0; ++cur_J; }
       slot = (slot + 1 == SLOTS) ? 0 : slot + 1;
     }
@@ -443,148 +658,90 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
   }
 }
 
-// Units of invalid problems: no loads; each segment publishes a zero partial (the finishing
-// kernel writes zeros for invalid problems anyway) and the error word is set.
-__device__ void run_invalid(const GemvParams &P, const Lds &sm, int ub, int ue) {
-  if (threadIdx.x == 0) __hip_atomic_fetch_or(P.errword, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Units of invalid problems (table mode): no loads; each segment publishes a zero partial
+// (the finish writes zeros for invalid problems anyway) and the error word is set.
+template <bool LIST>
+__device__ void run_invalid(const GemvParams &P, const Lds &sm, int p, int ub, int ue, int c, int q0) {
+  if (threadIdx.x == 0) __hip_atomic_fetch_or(P.errword, kErrBadEntry, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   floatx4 acc[8];
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int nI = nI_of<LIST>(P, p), base = units_base<LIST>(P, p), qb = blocks_base<LIST>(P, p);
   for (int u = ub; u < ue; ++u) {
-    const int q = u / P.nI, I = u - q * P.nI;
-    if (I == P.nI - 1 || u == ue - 1) publish_partial(P, sm, q, acc);
+    const int lu = u - base, J = lu / nI, I = lu - J * nI;
+    if (I == nI - 1 || u == ue - 1) publish_partial(P, sm, c, qb + J - q0, acc);
   }
 }
 
-// KS = 2, 3, 4: one layer of that width (no table, the K dispatch compiled away, a smaller
-// kernel); KS = 0: a list of problems with per-entry K.
-template <int KS, int CBS = 1>
-__global__ __launch_bounds__(kThreads, 4) void gemv_partial_kernel(GemvParams P) {
-  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
-  const Lds sm = lds_carve(lds_raw, P.L.B, P.kA);
-  // Top issue priority from the start: a workgroup dispatched after its CU's others are
-  // already decoding would otherwise run its prologue at the lowest priority, behind them.
-  __builtin_amdgcn_s_setprio(3);
-  // The arguments needed before the first code copy, read in one round trip (left alone,
-  // the compiler loads them in several dependent rounds around the early branches).
-  asm volatile("" ::"s"(P.U), "s"(P.G), "s"(P.nI), "s"(P.nJ), "s"(P.kA), "s"(P.L.B), "s"(P.L.in_features),
-               "s"(P.L.out_features), "s"(P.L.single.code), "s"(P.L.single.rin), "s"(P.L.single.s_in),
-               "s"(P.L.x), "s"(P.L.shared_side), "s"(P.L.shared_r), "s"(P.L.shared_s), "s"(P.partials), "s"(P.L.table), "s"(P.L.E),
-               "s"(P.L.routed));
-  const int g = blockIdx.x;
-  const int u0 = wg_start(g, P.U, P.G), u1 = wg_start(g + 1, P.U, P.G);
-  if constexpr (KS != 0) {
-    if (u0 < u1) run_problem<KS, CBS>(P, sm, get_problem<false>(P, 0), 0, u0, u1, true);
-    return;
-  }
-  const int per_problem = P.nI * P.nJ;
-  for (int u = u0; u < u1;) {
-    const int p = u / per_problem;
-    const int ue = min(u1, (p + 1) * per_problem);
-    const Problem pr = get_problem(P, p);
-    const bool fresh = u == u0;
-    switch (pr.ok ? pr.K + 4 * (pr.cb - 1) : 0) {
-      case 2: run_problem<2>(P, sm, pr, p, u, ue, fresh); break;
-      case 3: run_problem<3>(P, sm, pr, p, u, ue, fresh); break;
-      case 4: run_problem<4>(P, sm, pr, p, u, ue, fresh); break;
-      case 6: run_problem<2, 2>(P, sm, pr, p, u, ue, fresh); break;
-      case 7: run_problem<3, 2>(P, sm, pr, p, u, ue, fresh); break;
-      case 8: run_problem<4, 2>(P, sm, pr, p, u, ue, fresh); break;
-      default: run_invalid(P, sm, u, ue); break;
-    }
-    u = ue;
-  }
-}
+// ---------------------------------------------------------------------------------------
+// Finishing.
+// ---------------------------------------------------------------------------------------
 
-// One workgroup per column block q: sum the contributors' partials in workgroup order,
-// rotate, scale and write fp16 y.
-constexpr int kPartialBatch = 32;  // partial loads a thread issues together
-
-__global__ __launch_bounds__(kThreads) void gemv_finish_kernel(GemvParams P) {
-  __shared__ float fin[kMaxB][128];
-  // all arguments in one early round trip
-  asm volatile("" ::"s"(P.U), "s"(P.G), "s"(P.nI), "s"(P.nJ), "s"(P.maxseg), "s"(P.partials), "s"(P.L.B),
-               "s"(P.L.out_features), "s"(P.L.y), "s"(P.L.table), "s"(P.L.E), "s"(P.L.routed),
-               "s"(P.L.single.rout), "s"(P.L.single.s_out), "s"(P.L.shared_side), "s"(P.L.shared_r),
-               "s"(P.L.shared_s));
-  const int B = P.L.B, out = P.L.out_features;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q = blockIdx.x;
-  // Contributors g_lo..g_hi.  Every contributor after the first starts its range inside
-  // block q, so q is its first segment; only g_lo can reach q at a later segment.  The
-  // partial loads therefore need no table and no barrier: they are issued first.
-  const int g_lo = owner(q * P.nI, P.U, P.G), g_hi = owner((q + 1) * P.nI - 1, P.U, P.G);
-  const int seg_lo = q - wg_start(g_lo, P.U, P.G) / P.nI;
-  float v[kMaxB * 128 / kThreads];
+// Sums of column block q's partials at indexes idx_i = threadIdx.x + i * kThreads (i < NI,
+// idx < B*128), chunks added in chunk order starting from 0 -- the same order whoever runs
+// it.  Loads are device-scope and up to 32 are in flight per thread.
+template <bool LIST, int NI>
+__device__ __forceinline__ void block_sums(const GemvParams &P, int q, float (&v)[NI]) {
+  const int B = P.L.B;
+  const BlockChunks c = block_chunks<LIST>(P, q);
+  const __amdgpu_buffer_rsrc_t rp = buffer_rsrc(P.partials, P.partial_bytes);
+  constexpr int kBatch = 32 / NI;
 #pragma unroll
-  for (int i = 0; i < kMaxB * 128 / kThreads; ++i) v[i] = 0.f;
-  for (int gb = g_lo; gb <= g_hi; gb += kPartialBatch) {
+  for (int i = 0; i < NI; ++i) v[i] = 0.f;
+  for (int gb = c.lo; gb <= c.hi; gb += kBatch) {
+    float part[NI][kBatch];
 #pragma unroll
-    for (int i = 0; i < kMaxB * 128 / kThreads; ++i) {
-      const int idx = tid + i * kThreads;
-      if (idx < B * 128) {
-        float part[kPartialBatch];
+    for (int t = 0; t < kBatch; ++t) {
+      const int gg = gb + t;
+      const uint32_t slot = (uint32_t)(gg * P.maxseg + (gg == c.lo ? c.seg_lo : 0));
 #pragma unroll
-        for (int t = 0; t < kPartialBatch; ++t) {
-          const int gg = gb + t;
-          const size_t sl = (size_t)gg * P.maxseg + (gg == g_lo ? seg_lo : 0);
-          part[t] = gg <= g_hi ? P.partials[sl * kMaxB * 128 + idx] : 0.f;
-        }
-#pragma unroll
-        for (int t = 0; t < kPartialBatch; ++t) v[i] += part[t];
+      for (int i = 0; i < NI; ++i) {
+        const int idx = threadIdx.x + i * kThreads;
+        part[i][t] = 0.f;
+        if (gg <= c.hi && idx < B * 128)
+          part[i][t] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(rp, (slot * B * 128 + idx) * 4, 0, kSC1));
       }
     }
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) v[i] += part[i][t];
   }
-  // the output-side vectors (their loads overlap the partials')
-  const int p = q / P.nJ, J = q - p * P.nJ;
-  const Problem pr = get_problem(P, p);
+}
+
+// Output-side scales of columns J*128 + lane and + 64 (rout * s_out * the remaining factor).
+__device__ __forceinline__ float2 out_scales(const uint16_t *rout, const float *s_out, int J, int lane) {
   const int c0 = J * 128 + lane, c1 = c0 + 64;
-  float sa = 0.f, sb = 0.f;
-  if (pr.ok) {
-    sa = h2f(ldg(pr.rout + c0)) * (1.0f / 128.0f);
-    sb = h2f(ldg(pr.rout + c1)) * (1.0f / 128.0f);
-    if (pr.s_out) { sa *= ldg(pr.s_out + c0); sb *= ldg(pr.s_out + c1); }
-  }
+  float sa = h2f(ldg(rout + c0)) * kOutScale, sb = h2f(ldg(rout + c1)) * kOutScale;
+  if (s_out) { sa *= ldg(s_out + c0); sb *= ldg(s_out + c1); }
+  return float2{sa, sb};
+}
+
+template <bool LIST>
+__device__ void finish_plain(const GemvParams &P, const Lds &sm, int q) {
+  const int B = P.L.B;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int p = problem_of_block<LIST>(P, q), J = q - blocks_base<LIST>(P, p);
+  const Problem pr = get_problem<LIST>(P, p);
+  float2 sc = {0.f, 0.f};
+  if (pr.ok) sc = out_scales(pr.rout, pr.s_out, J, lane);
+  float v[kMaxB * 128 / kThreads];
+  block_sums<LIST>(P, q, v);
 #pragma unroll
   for (int i = 0; i < kMaxB * 128 / kThreads; ++i) {
     const int idx = tid + i * kThreads;
-    if (idx < B * 128) fin[idx >> 7][idx & 127] = v[i];
+    if (idx < B * 128) sm.red[idx] = v[i];
   }
   __syncthreads();
-  uint16_t *y = P.L.y + (size_t)p * B * out;
+  const int c0 = J * 128 + lane;
   for (int b = wave; b < B; b += kWaves) {
-    float va = fin[b][lane], vb = fin[b][lane + 64];
-    if (pr.ok) {
-      wave_fwht128(va, vb);
-      va *= sa;
-      vb *= sb;
-    } else {
-      va = 0.f;
-      vb = 0.f;
-    }
-    y[(size_t)b * out + c0] = f2h(va);
-    y[(size_t)b * out + c1] = f2h(vb);
+    float va = sm.red[b * 128 + lane], vb = sm.red[b * 128 + lane + 64];
+    wave_fwht128(va, vb);
+    pr.y[(size_t)b * pr.out + c0] = f2h(va * sc.x);       // (an invalid problem has zero scales)
+    pr.y[(size_t)b * pr.out + c0 + 64] = f2h(vb * sc.y);
   }
-}
-
-// Batch row 0 of column block q, column c: the contributors' partials added in workgroup
-// order (the order gemv_finish_kernel uses).
-__device__ __forceinline__ float partial_sum_b1(const GemvParams &P, int q, int c) {
-  const int g_lo = owner(q * P.nI, P.U, P.G), g_hi = owner((q + 1) * P.nI - 1, P.U, P.G);
-  const int seg_lo = q - wg_start(g_lo, P.U, P.G) / P.nI;
-  float v = 0.f;
-  for (int gb = g_lo; gb <= g_hi; gb += kPartialBatch) {
-    float part[kPartialBatch];
-#pragma unroll
-    for (int t = 0; t < kPartialBatch; ++t) {
-      const int gg = gb + t;
-      const size_t sl = (size_t)gg * P.maxseg + (gg == g_lo ? seg_lo : 0);
-      part[t] = gg <= g_hi ? P.partials[sl * kMaxB * 128 + c] : 0.f;
-    }
-#pragma unroll
-    for (int t = 0; t < kPartialBatch; ++t) v += part[t];
-  }
-  return v;
+  __syncthreads();
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z) ("EXLR8" page, calibration paragraph: the
@@ -592,72 +749,199 @@ __device__ __forceinline__ float partial_sum_b1(const GemvParams &P, int q, int 
 // +inf in fp32 and the quotient is -0, the limit.
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-// kFinishSwiGLU, B = 1.  Workgroup f handles output block J of slice h of routed slot k
-// (f = (k*H + h)*nJ + J): threads 0..127 sum the gate entry's partials, threads 128..255
-// the up entry's; waves 0 and 2 rotate and scale them; then a = silu(g) * u is written as
-// fp16 to y[k][(h*nJ + J)*128 + c].
-__global__ __launch_bounds__(kThreads) void gemv_finish_swiglu_kernel(GemvParams P) {
-  __shared__ float gu[2][128];
+// kFinishSwiGLU, B = 1.  Group f = (slot*H + h)*nJ + J: threads 0..127 sum the gate
+// entry's partials, threads 128..255 the up entry's; waves 0 and 2 rotate and scale them;
+// then a = silu(g) * u is written as fp16 to y[slot][(h*nJ + J)*128 + c].
+__device__ void finish_swiglu(const GemvParams &P, const Lds &sm, int f) {
   const int H = P.L.halves, nJ = P.nJ;
-  const int f = blockIdx.x;
   const int slot = f / (H * nJ), rem = f - slot * H * nJ;
   const int pg = slot * 2 * H + rem / nJ, J = rem - (rem / nJ) * nJ;
   const int tid = threadIdx.x, c = tid & 127, which = tid >> 7, lane = tid & 63;
   const int p = which ? pg + H : pg;
-  const float v = partial_sum_b1(P, p * nJ + J, c);
   const bool rot = (tid & 127) < 64;  // waves 0 (gate) and 2 (up)
-  float sa = 0.f, sb = 0.f;
+  float2 sc = {0.f, 0.f};
   if (rot) {
-    const Problem pr = get_problem(P, p);
-    if (pr.ok) {
-      const int c0 = J * 128 + lane, c1 = c0 + 64;
-      sa = h2f(ldg(pr.rout + c0)) * (1.0f / 128.0f);
-      sb = h2f(ldg(pr.rout + c1)) * (1.0f / 128.0f);
-      if (pr.s_out) { sa *= ldg(pr.s_out + c0); sb *= ldg(pr.s_out + c1); }
-    }
+    const Problem pr = get_problem<false>(P, p);
+    if (pr.ok) sc = out_scales(pr.rout, pr.s_out, J, lane);  // (an invalid entry's output is zero)
   }
-  gu[which][c] = v;
+  // each half of the workgroup sums one block: thread t of the half takes column t
+  const BlockChunks cb = block_chunks<false>(P, p * nJ + J);
+  const __amdgpu_buffer_rsrc_t rp = buffer_rsrc(P.partials, P.partial_bytes);
+  float v = 0.f;
+  for (int gb = cb.lo; gb <= cb.hi; gb += 32) {
+    float part[32];
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const int gg = gb + t;
+      const uint32_t s = (uint32_t)(gg * P.maxseg + (gg == cb.lo ? cb.seg_lo : 0));
+      part[t] = gg <= cb.hi ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, (s * 128 + c) * 4, 0, kSC1))
+                           : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < 32; ++t) v += part[t];
+  }
+  float *gu = sm.red;  // [2][128]
+  gu[which * 128 + c] = v;
   __syncthreads();
   if (rot) {
-    float va = gu[which][lane], vb = gu[which][lane + 64];
+    float va = gu[which * 128 + lane], vb = gu[which * 128 + lane + 64];
     wave_fwht128(va, vb);
-    gu[which][lane] = va * sa;  // (an invalid entry has sa = sb = 0: its output is zero)
-    gu[which][lane + 64] = vb * sb;
+    gu[which * 128 + lane] = va * sc.x;
+    gu[which * 128 + lane + 64] = vb * sc.y;
   }
   __syncthreads();
   if (tid < 128) {
     const int inter = H * nJ * 128;
-    P.L.y[(size_t)slot * inter + rem * 128 + c] = f2h(silu(gu[0][c]) * gu[1][c]);
+    P.L.y[(size_t)slot * inter + rem * 128 + c] = f2h(silu(gu[c]) * gu[128 + c]);
+  }
+  __syncthreads();
+}
+
+// kFinishWeighted, B = 1.  Group J: thread (r, c) (r = tid / 128) adds w[k] * (sum of
+// problem k's partials of block J) over k = r, r + 2, ..., in that order; the two sums are
+// added in r order, rotated once and scaled by the shared sv.
+__device__ void finish_weighted(const GemvParams &P, const Lds &sm, int J) {
+  const int tid = threadIdx.x, c = tid & 127, r = tid >> 7, lane = tid & 63;
+  const int nJ = P.nJ, n = P.L.n_problems;
+  const __amdgpu_buffer_rsrc_t rp = buffer_rsrc(P.partials, P.partial_bytes);
+  float acc = 0.f;
+  for (int k = r; k < n; k += 2) {
+    const int q = k * nJ + J;
+    const BlockChunks cb = block_chunks<false>(P, q);
+    float v = 0.f;
+    for (int gb = cb.lo; gb <= cb.hi; gb += 32) {
+      float part[32];
+#pragma unroll
+      for (int t = 0; t < 32; ++t) {
+        const int gg = gb + t;
+        const uint32_t s = (uint32_t)(gg * P.maxseg + (gg == cb.lo ? cb.seg_lo : 0));
+        part[t] = gg <= cb.hi ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, (s * 128 + c) * 4, 0, kSC1))
+                             : 0.f;
+      }
+#pragma unroll
+      for (int t = 0; t < 32; ++t) v += part[t];
+    }
+    acc += ldg(P.L.router_w + k) * v;
+  }
+  sm.red[r * 128 + c] = acc;
+  __syncthreads();
+  if (tid < 64) {
+    float va = sm.red[lane] + sm.red[128 + lane];
+    float vb = sm.red[lane + 64] + sm.red[128 + lane + 64];
+    const float2 sc = out_scales(P.L.shared_r, P.L.shared_s, J, lane);
+    wave_fwht128(va, vb);
+    P.L.y[J * 128 + lane] = f2h(va * sc.x);
+    P.L.y[J * 128 + lane + 64] = f2h(vb * sc.y);
+  }
+  __syncthreads();
+}
+
+// End of chunk c: count the chunk in at the finish group of each of its segments; finish
+// the groups whose count this brings to the number of chunks covering them, and reset their
+// counters.  The workgroup's next chunk is taken from the queue in the same round trip and
+// left in *next (LDS).
+template <bool LIST>
+__device__ void arrive_chunk(const GemvParams &P, const Lds &sm, int c, int *next) {
+  const int cu0 = chunk_start(P, c), cu1 = chunk_end(P, c);
+  const int q0 = block_of_unit<LIST>(P, cu0), q1 = block_of_unit<LIST>(P, cu1 - 1);
+  __builtin_amdgcn_s_setprio(3);  // the arrivals and finishes ahead of other workgroups' decode
+  // Every thread's partial stores have completed before any counter moves (a workgroup
+  // barrier does not wait for global stores), so an arrival publishes complete partials.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  uint32_t *flags = sm.tiles;  // (the code ring is idle between chunks)
+  // the last thread of the workgroup takes the next chunk number (q1 - q0 < kThreads - 1
+  // whenever a chunk meets fewer column blocks than a workgroup has threads; otherwise it
+  // waits for the first round below)
+  uint32_t got = 0;
+  if (threadIdx.x == kThreads - 1 && P.n_chunks > P.G)
+    got = __hip_atomic_fetch_add(P.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int base = q0; base <= q1; base += kThreads) {
+    const int q = base + (int)threadIdx.x;
+    if (q <= q1) {
+      const int f = group_of_block<LIST>(P, q);
+      const uint32_t old = __hip_atomic_fetch_add(P.counters + f, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      flags[threadIdx.x] = old + 1 == (uint32_t)group_arrivals<LIST>(P, f) ? 1u : 0u;
+    }
+    if (base == q0 && threadIdx.x == kThreads - 1) *next = P.n_chunks > P.G ? (int)got + P.G : P.n_chunks;
+    __syncthreads();
+    const int cnt = min(kThreads, q1 - base + 1);
+    for (int i = 0; i < cnt; ++i) {
+      if (__builtin_amdgcn_readfirstlane(flags[i])) {
+        const int f = group_of_block<LIST>(P, base + i);
+        // The other chunks' partials are read after their arrivals were seen, with
+        // device-scope (sc1) loads, which read the coherent copy (the per-XCD L2s hold no
+        // stale one): no cache invalidation is needed.
+        if (LIST || P.L.finish == kFinishPlain) finish_plain<LIST>(P, sm, f);
+        else if (P.L.finish == kFinishSwiGLU) finish_swiglu(P, sm, f);
+        else finish_weighted(P, sm, f);
+        if (threadIdx.x == 0) __hip_atomic_store(P.counters + f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
   }
 }
 
-// kFinishWeighted, B = 1.  Workgroup J: thread (r, c) (r = tid / 128, 8 of them) adds
-// w[k] * (sum of problem k's partials of block J) over k = r, r + 8, ..., in that order;
-// the eight sums are then added in r order, rotated once and scaled by the shared sv.
-constexpr int kWeightedThreads = 1024;
-__global__ __launch_bounds__(kWeightedThreads) void gemv_finish_weighted_kernel(GemvParams P) {
-  __shared__ float red[kWeightedThreads / 128][128];
-  const int tid = threadIdx.x, c = tid & 127, r = tid >> 7, lane = tid & 63;
-  const int J = blockIdx.x, nJ = P.nJ, n = P.L.n_problems;
-  float acc = 0.f;
-  for (int k = r; k < n; k += kWeightedThreads / 128) acc += ldg(P.L.router_w + k) * partial_sum_b1(P, k * nJ + J, c);
-  red[r][c] = acc;
-  __syncthreads();
-  if (tid < 64) {
-    float va = 0.f, vb = 0.f;
-#pragma unroll
-    for (int i = 0; i < kWeightedThreads / 128; ++i) {
-      va += red[i][lane];
-      vb += red[i][lane + 64];
+// The units [cu0, cu1) of one chunk, problem by problem.
+template <bool LIST, int KS, int CBS>
+__device__ __forceinline__ void run_chunk(const GemvParams &P, const Lds &sm, int c, bool fresh) {
+  const int cu0 = chunk_start(P, c), cu1 = chunk_end(P, c);
+  const int q0 = block_of_unit<LIST>(P, cu0);
+  for (int u = cu0; u < cu1;) {
+    const int p = problem_of_unit<LIST>(P, u);
+    const int ue = min(cu1, units_base<LIST>(P, p + 1));
+    const Problem pr = get_problem<LIST>(P, p);
+    const bool f = fresh && u == cu0;
+    if constexpr (KS != 0) {
+      run_problem<KS, CBS, LIST>(P, sm, pr, p, u, ue, c, q0, f);
+    } else {
+      const int sel = pr.ok ? pr.K + 4 * (pr.cb - 1) : 0;
+      if (sel == 2) run_problem<2, 1, LIST>(P, sm, pr, p, u, ue, c, q0, f);
+      else if (sel == 3) run_problem<3, 1, LIST>(P, sm, pr, p, u, ue, c, q0, f);
+      else if (sel == 4) run_problem<4, 1, LIST>(P, sm, pr, p, u, ue, c, q0, f);
+      else if (CBS == 0 && sel == 6) run_problem<2, 2, LIST>(P, sm, pr, p, u, ue, c, q0, f);
+      else if (CBS == 0 && sel == 7) run_problem<3, 2, LIST>(P, sm, pr, p, u, ue, c, q0, f);
+      else if (CBS == 0 && sel == 8) run_problem<4, 2, LIST>(P, sm, pr, p, u, ue, c, q0, f);
+      else run_invalid<LIST>(P, sm, p, u, ue, c, q0);
     }
-    const int c0 = J * 128 + lane, c1 = c0 + 64;
-    float sa = h2f(ldg(P.L.shared_r + c0)) * (1.0f / 128.0f);
-    float sb = h2f(ldg(P.L.shared_r + c1)) * (1.0f / 128.0f);
-    if (P.L.shared_s) { sa *= ldg(P.L.shared_s + c0); sb *= ldg(P.L.shared_s + c1); }
-    wave_fwht128(va, vb);
-    P.L.y[c0] = f2h(va * sa);
-    P.L.y[c1] = f2h(vb * sb);
+    u = ue;
   }
+}
+
+// LIST: list mode.  KS = 2, 3, 4: every problem has that width and codebook CBS (the K
+// dispatch compiled away, a smaller kernel); KS = 0: per-problem K, with CBS = 1 (every
+// problem on the MCG codebook) or 0 (either codebook).
+template <bool LIST, int KS, int CBS>
+__global__ __launch_bounds__(kThreads, 4) void gemv_kernel(GemvParams P) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  __shared__ int next_chunk;
+  const Lds sm = lds_carve(lds_raw, P.L.B, P.kA);
+  int c = blockIdx.x;  // (the launch keeps G <= n_chunks)
+  for (bool fresh = true;; fresh = false) {
+    // Top issue priority for the chunk's set-up: its loads go out while other workgroups on
+    // the CU decode (and a workgroup dispatched after its CU's others are already decoding
+    // would otherwise run its prologue at the lowest priority, behind them).
+    __builtin_amdgcn_s_setprio(3);
+    run_chunk<LIST, KS, CBS>(P, sm, c, fresh);
+    arrive_chunk<LIST>(P, sm, c, &next_chunk);
+    c = next_chunk;
+    if (c >= P.n_chunks) break;
+  }
+  // The last workgroup to leave resets the queue for the next call (every workgroup has taken
+  // its last chunk number before it counts itself out).
+  if (threadIdx.x == 0 && P.n_chunks > P.G) {
+    const uint32_t done = __hip_atomic_fetch_add(P.queue + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == (uint32_t)P.G - 1) {
+      __hip_atomic_store(P.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(P.queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// An empty weighted sum (no routed experts): y = 0.
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint16_t *y, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) y[i] = 0;
 }
 
 struct DeviceInfo {
@@ -677,7 +961,7 @@ int device_cus_and_occupancy(int B, int *cus_out) {
   }
   if (d.occ[B] == 0) {
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_partial_kernel<0>, kThreads,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_kernel<false, 0, 0>, kThreads,
                                                      lds_bytes(B, kWaves * kMaxTasks / B)) != hipSuccess ||
         occ <= 0)
       occ = 2;
@@ -688,133 +972,193 @@ int device_cus_and_occupancy(int B, int *cus_out) {
 }
 
 struct Geometry {
-  int U, G, nI, nJ, maxseg, nq, kA;
-  size_t partials_off, bytes;
+  bool ok = false;
+  int U = 0, G = 0, CH = 0, CHs = 0, big_units = 0, n_chunks = 0, maxseg = 0, kA = 0, nq = 0, nf = 0;
+  int ubase[kMaxList + 1] = {}, qbase[kMaxList + 1] = {};
+  size_t partial_bytes = 0, bytes = 0;
 };
 
-Geometry geometry(int n_problems, int in_features, int out_features, int B) {
+// The share of the units left to the small chunks, and their size.  Measured on the dense
+// MLP step, every tail share tried (5-30%, chunks of 1-4 units) was slower than none: each
+// small chunk pays the set-up latency of its rotation and first code copies (a few
+// microseconds) at the end of the launch, where few workgroups remain to cover it.  The
+// default is therefore one equal static share per workgroup; the tail stays available.
+constexpr double kTailShare = 0.0;
+constexpr int kSmallChunk = 2;
+constexpr int kMaxChunk = 32;
+
+Geometry geometry(const GemvLaunch &a) {
   Geometry gm;
-  gm.nI = in_features / 128;
-  gm.nJ = out_features / 128;
-  gm.nq = n_problems * gm.nJ;
-  const long long U = (long long)gm.nq * gm.nI;
+  const int B = a.B < 1 ? 1 : (a.B > kMaxB ? kMaxB : a.B);
+  long long U = 0, nq = 0;
+  int nI_min = INT_MAX;
+  if (a.table == nullptr) {
+    for (int p = 0; p < a.n_list; ++p) {
+      gm.ubase[p] = (int)U;
+      gm.qbase[p] = (int)nq;
+      const int nI = a.list[p].L.in_features / 128, nJ = a.list[p].L.out_features / 128;
+      U += (long long)nI * nJ;
+      nq += nJ;
+      nI_min = nI < nI_min ? nI : nI_min;
+    }
+    for (int p = a.n_list; p <= kMaxList; ++p) {
+      gm.ubase[p] = (int)(U < INT_MAX ? U : INT_MAX);
+      gm.qbase[p] = (int)(nq < INT_MAX ? nq : INT_MAX);
+    }
+  } else {
+    const int nI = a.in_features / 128, nJ = a.out_features / 128;
+    U = (long long)a.n_problems * nI * nJ;
+    nq = (long long)a.n_problems * nJ;
+    nI_min = nI;
+  }
+  if (U <= 0 || U >= (1LL << 31) || nq > kMaxFinishGroups) return gm;
   gm.U = (int)U;
+  gm.nq = (int)nq;
+  gm.nf = a.table && a.finish == kFinishSwiGLU ? gm.nq / 2
+        : a.table && a.finish == kFinishWeighted ? a.out_features / 128 : gm.nq;
   int cus = 0;
   const int occ = device_cus_and_occupancy(B, &cus);
   long long G = (long long)cus * occ;
-  // Debug/test override of the workgroup count (exercises ranges that span column blocks).
+  // Debug/test overrides of the workgroup count and the chunk size (they exercise chunks
+  // that span column blocks and problems, and many chunks per workgroup).
   if (const char *env = getenv("TRELLIS_GEMV_WGS")) {
     const long long v = atoll(env);
     if (v > 0) G = v;
   }
   if (G > U) G = U;
   if (G < 1) G = 1;
+  // The big chunks take (1 - tail) of the units in equal shares, the small ones the rest.
+  double tail = kTailShare;
+  if (const char *env = getenv("TRELLIS_GEMV_TAIL")) tail = atof(env);
+  if (tail < 0) tail = 0;
+  if (tail > 1) tail = 1;
+  long long CH = (long long)((double)U * (1.0 - tail) / (double)G);
+  if (tail == 0) CH = (U + G - 1) / G;
+  if (CH < 1) CH = 1;
+  long long CHs = kSmallChunk;
+  if (const char *env = getenv("TRELLIS_GEMV_CHUNK")) {
+    const long long v = atoll(env);
+    if (v > 0) CHs = v;
+  }
+  if (CHs > kMaxChunk) CHs = kMaxChunk;
+  const long long big = U < G * CH ? U : G * CH;
+  gm.CH = (int)CH;
+  gm.CHs = (int)CHs;
+  gm.big_units = (int)big;
+  // every workgroup owns one big chunk, so none may be empty
+  G = (big + CH - 1) / CH;
   gm.G = (int)G;
-  const long long per = (U + G - 1) / G;
-  gm.maxseg = (int)((per + gm.nI - 1) / gm.nI + 1);
+  gm.n_chunks = (int)(G + (U - big + CHs - 1) / CHs);
+  // a chunk of n units meets at most (n - 1) / nI_min + 2 column blocks
+  const long long chmax = CH > CHs ? CH : CHs;
+  const long long maxseg = (chmax - 1) / nI_min + 2;
+  gm.maxseg = (int)(maxseg < nq ? maxseg : nq);
   long long kA_max = kABudget / (512 * B);
   if (kA_max > (long long)kWaves * kMaxTasks / B) kA_max = (long long)kWaves * kMaxTasks / B;
-  gm.kA = (int)(per < kA_max ? per : kA_max);
-  gm.partials_off = 256;
-  gm.bytes = gm.partials_off + (size_t)gm.G * gm.maxseg * kMaxB * 128 * sizeof(float);
+  gm.kA = (int)(chmax < kA_max ? chmax : kA_max);
+  gm.partial_bytes = (size_t)gm.n_chunks * gm.maxseg * B * 128 * sizeof(float);
+  if (gm.partial_bytes >= (1ULL << 31)) return gm;  // 32-bit buffer offsets
+  gm.bytes = kWsReserved + gm.partial_bytes;
+  gm.ok = true;
   return gm;
-}
-
-}  // namespace
-
-int gemv_max_column_blocks() { return 1 << 30; }
-
-size_t gemv_workspace_bytes(int n_problems, int in_features, int out_features, int B) {
-  if (n_problems <= 0) return 256;
-  if (B < 1) B = 1;
-  if (B > kMaxB) B = kMaxB;
-  return geometry(n_problems, in_features, out_features, B).bytes;
-}
-
-namespace {
-
-// The partial and finishing launches of one problem list, with the error word and the
-// partials region given separately (the routed MLP places two lists in one workspace).
-hipError_t launch_gemv_parts(const GemvLaunch &a, uint32_t *errword, float *partials, size_t partial_bytes,
-                             hipStream_t stream) {
-  if (a.B < 1 || a.B > kMaxB) return hipErrorInvalidValue;
-  if (a.finish != kFinishPlain && a.B != 1) return hipErrorInvalidValue;
-  if (a.n_problems <= 0) {
-    if (a.finish != kFinishWeighted) return hipSuccess;
-    // an empty weighted sum: y = 0 (the finishing kernel reads no partials)
-    GemvParams P{};
-    P.L = a;
-    P.L.n_problems = 0;
-    P.nJ = a.out_features / 128;
-    gemv_finish_weighted_kernel<<<P.nJ, kWeightedThreads, 0, stream>>>(P);
-    return hipGetLastError();
-  }
-  const long long units = (long long)a.n_problems * (a.out_features / 128) * (a.in_features / 128);
-  if (units >= (1LL << 31)) return hipErrorInvalidValue;
-  const Geometry gm = geometry(a.n_problems, a.in_features, a.out_features, a.B);
-  if (partial_bytes < gm.bytes - gm.partials_off) return hipErrorInvalidValue;
-  if ((long long)gm.G * gm.U >= (1LL << 32)) return hipErrorInvalidValue;  // 32-bit slot arithmetic
-  GemvParams P;
-  P.L = a;
-  if (P.L.group < 1) P.L.group = 1;
-  P.errword = errword;
-  P.partials = partials;
-  P.U = gm.U;
-  P.G = gm.G;
-  P.nI = gm.nI;
-  P.nJ = gm.nJ;
-  P.maxseg = gm.maxseg;
-  P.kA = gm.kA;
-  const size_t lds = lds_bytes(a.B, gm.kA);
-  const int single = a.table == nullptr ? a.single.K + 4 * (a.single.cb - 1) : 0;
-  if (single == 2) gemv_partial_kernel<2><<<gm.G, kThreads, lds, stream>>>(P);
-  else if (single == 3) gemv_partial_kernel<3><<<gm.G, kThreads, lds, stream>>>(P);
-  else if (single == 4) gemv_partial_kernel<4><<<gm.G, kThreads, lds, stream>>>(P);
-  else if (single == 6) gemv_partial_kernel<2, 2><<<gm.G, kThreads, lds, stream>>>(P);
-  else if (single == 7) gemv_partial_kernel<3, 2><<<gm.G, kThreads, lds, stream>>>(P);
-  else if (single == 8) gemv_partial_kernel<4, 2><<<gm.G, kThreads, lds, stream>>>(P);
-  else gemv_partial_kernel<0><<<gm.G, kThreads, lds, stream>>>(P);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.finish == kFinishSwiGLU) gemv_finish_swiglu_kernel<<<gm.nq / 2, kThreads, 0, stream>>>(P);
-  else if (a.finish == kFinishWeighted) gemv_finish_weighted_kernel<<<gm.nJ, kWeightedThreads, 0, stream>>>(P);
-  else gemv_finish_kernel<<<gm.nq, kThreads, 0, stream>>>(P);
-  return hipGetLastError();
 }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// The kernel launch of one problem list whose partials go to `partials` (the error word
+// and the counters are the workspace's reserved region at `ws`).
+hipError_t launch_list(const GemvLaunch &a, char *ws, float *partials, size_t partial_room, hipStream_t stream) {
+  if (a.B < 1 || a.B > kMaxB) return hipErrorInvalidValue;
+  if (a.table && a.finish != kFinishPlain && a.B != 1) return hipErrorInvalidValue;
+  if (!a.table && (a.n_list < 1 || a.n_list > kMaxList)) return hipErrorInvalidValue;
+  const Geometry gm = geometry(a);
+  if (!gm.ok || partial_room < gm.partial_bytes) return hipErrorInvalidValue;
+  GemvParams P;
+  P.L = a;
+  if (P.L.group < 1) P.L.group = 1;
+  P.errword = reinterpret_cast<uint32_t *>(ws);
+  P.queue = reinterpret_cast<uint32_t *>(ws + kWsQueueOffset);
+  P.counters = reinterpret_cast<uint32_t *>(ws + kWsHeaderBytes);
+  P.partials = partials;
+  P.partial_bytes = (long long)gm.partial_bytes;
+  P.U = gm.U;
+  P.CH = gm.CH;
+  P.CHs = gm.CHs;
+  P.big_units = gm.big_units;
+  P.n_chunks = gm.n_chunks;
+  P.G = gm.G;
+  P.maxseg = gm.maxseg;
+  P.kA = gm.kA;
+  P.nI = a.table ? a.in_features / 128 : 0;
+  P.nJ = a.table ? a.out_features / 128 : 0;
+  for (int i = 0; i <= kMaxList; ++i) {
+    P.ubase[i] = gm.ubase[i];
+    P.qbase[i] = gm.qbase[i];
+  }
+  const size_t lds = lds_bytes(a.B, gm.kA);
+  if (a.table) {
+    gemv_kernel<false, 0, 0><<<gm.G, kThreads, lds, stream>>>(P);
+    return hipGetLastError();
+  }
+  // list mode: a kernel specialised for one width when every layer shares it
+  bool same = true, all_mcg = true;
+  for (int p = 0; p < a.n_list; ++p) {
+    same = same && a.list[p].L.K == a.list[0].L.K && a.list[p].L.cb == a.list[0].L.cb;
+    all_mcg = all_mcg && a.list[p].L.cb == 1;
+  }
+  const int sel = same ? a.list[0].L.K + 4 * (a.list[0].L.cb - 1) : (all_mcg ? 1 : 0);
+  switch (sel) {
+    case 2: gemv_kernel<true, 2, 1><<<gm.G, kThreads, lds, stream>>>(P); break;
+    case 3: gemv_kernel<true, 3, 1><<<gm.G, kThreads, lds, stream>>>(P); break;
+    case 4: gemv_kernel<true, 4, 1><<<gm.G, kThreads, lds, stream>>>(P); break;
+    case 6: gemv_kernel<true, 2, 2><<<gm.G, kThreads, lds, stream>>>(P); break;
+    case 7: gemv_kernel<true, 3, 2><<<gm.G, kThreads, lds, stream>>>(P); break;
+    case 8: gemv_kernel<true, 4, 2><<<gm.G, kThreads, lds, stream>>>(P); break;
+    case 1: gemv_kernel<true, 0, 1><<<gm.G, kThreads, lds, stream>>>(P); break;
+    default: gemv_kernel<true, 0, 0><<<gm.G, kThreads, lds, stream>>>(P); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
+size_t gemv_workspace_bytes(const GemvLaunch &a) {
+  const bool empty = a.table ? a.n_problems <= 0 : a.n_list <= 0;
+  if (empty) return kWsReserved;
+  const Geometry gm = geometry(a);
+  return gm.ok ? gm.bytes : 0;
+}
+
+size_t gemv_workspace_bytes(int n_problems, int in_features, int out_features, int B) {
+  GemvLaunch a{};
+  a.table = reinterpret_cast<const trellis_linear *>(1);  // (only the mode matters here)
+  a.n_problems = n_problems;
+  a.in_features = in_features;
+  a.out_features = out_features;
+  a.B = B;
+  return gemv_workspace_bytes(a);
+}
+
 hipError_t launch_gemv(const GemvLaunch &a, void *ws, size_t ws_bytes, hipStream_t stream) {
-  if (a.n_problems <= 0 && a.finish != kFinishWeighted) return hipSuccess;
-  const size_t need = gemv_workspace_bytes(a.n_problems, a.in_features, a.out_features, a.B);
-  if (ws_bytes < need) return hipErrorInvalidValue;
+  const bool empty = a.table ? a.n_problems <= 0 : a.n_list <= 0;
+  if (empty) {
+    if (!(a.table && a.finish == kFinishWeighted)) return hipSuccess;
+    // an empty weighted sum: y = 0
+    const int n = a.out_features;
+    zero_fill_kernel<<<(n + 255) / 256, 256, 0, stream>>>(a.y, n);
+    return hipGetLastError();
+  }
+  const size_t need = gemv_workspace_bytes(a);
+  if (need == 0 || ws_bytes < need) return hipErrorInvalidValue;
   char *w = static_cast<char *>(ws);
-  return launch_gemv_parts(a, reinterpret_cast<uint32_t *>(w), reinterpret_cast<float *>(w + 256), ws_bytes - 256,
-                           stream);
+  return launch_list(a, w, reinterpret_cast<float *>(w + kWsReserved), ws_bytes - kWsReserved, stream);
 }
 
-// Workspace of the routed MLP: [error word: 256 B][activations fp16 [n][inter], 256-aligned]
+// Workspace of the routed MLP: [reserved region][activations fp16 [n][inter], 256-aligned]
 // [partials: the larger of the two launches' regions].  The down launch reuses the gate/up
-// partials region: it runs after the gate/up finishing kernel on the same stream.
-size_t moe_mlp_workspace_bytes(int hidden, int inter, int halves, int n) {
-  if (n <= 0) return 256;
-  const size_t gu = gemv_workspace_bytes(n * 2 * halves, hidden, inter / halves, 1) - 256;
-  const size_t d = gemv_workspace_bytes(n, inter, hidden, 1) - 256;
-  return 256 + align256((size_t)n * inter * 2) + (gu > d ? gu : d);
-}
-
-hipError_t launch_moe_mlp(const MlpLaunch &m, void *ws, size_t ws_bytes, hipStream_t stream) {
-  const size_t need = moe_mlp_workspace_bytes(m.hidden, m.inter, m.halves, m.n);
-  if (ws_bytes < need) return hipErrorInvalidValue;
-  char *w = static_cast<char *>(ws);
-  uint32_t *errword = reinterpret_cast<uint32_t *>(w);
-  const size_t act_bytes = m.n > 0 ? align256((size_t)m.n * m.inter * 2) : 0;
-  uint16_t *act = m.act ? m.act : reinterpret_cast<uint16_t *>(w + 256);
-  float *partials = reinterpret_cast<float *>(w + 256 + act_bytes);
-  const size_t partial_bytes = ws_bytes - 256 - act_bytes;
-
+// partials region: it runs after the gate/up launch on the same stream.
+namespace {
+GemvLaunch mlp_gate_up(const MlpLaunch &m, uint16_t *act) {
   GemvLaunch gu{};
   gu.table = m.gate_up;
   gu.E = m.E;
@@ -832,10 +1176,9 @@ hipError_t launch_moe_mlp(const MlpLaunch &m, void *ws, size_t ws_bytes, hipStre
   gu.shared_side = 0;
   gu.finish = kFinishSwiGLU;
   gu.halves = m.halves;
-  if (m.n > 0) {
-    const hipError_t e = launch_gemv_parts(gu, errword, partials, partial_bytes, stream);
-    if (e != hipSuccess) return e;
-  }
+  return gu;
+}
+GemvLaunch mlp_down(const MlpLaunch &m, const uint16_t *act) {
   GemvLaunch d{};
   d.table = m.down;
   d.E = m.E;
@@ -853,7 +1196,40 @@ hipError_t launch_moe_mlp(const MlpLaunch &m, void *ws, size_t ws_bytes, hipStre
   d.shared_side = 1;
   d.finish = kFinishWeighted;
   d.router_w = m.router_w;
-  return launch_gemv_parts(d, errword, partials, partial_bytes, stream);
+  return d;
+}
+}  // namespace
+
+size_t moe_mlp_workspace_bytes(int hidden, int inter, int halves, int n) {
+  if (n <= 0) return kWsReserved;
+  MlpLaunch m{};
+  m.hidden = hidden;
+  m.inter = inter;
+  m.halves = halves;
+  m.n = n;
+  m.gate_up = m.down = reinterpret_cast<const trellis_linear *>(1);  // (only the mode matters here)
+  const size_t gu = gemv_workspace_bytes(mlp_gate_up(m, nullptr));
+  const size_t d = gemv_workspace_bytes(mlp_down(m, nullptr));
+  if (gu == 0 || d == 0) return 0;
+  const size_t room = (gu > d ? gu : d) - kWsReserved;
+  return kWsReserved + align256((size_t)n * inter * 2) + room;
+}
+
+hipError_t launch_moe_mlp(const MlpLaunch &m, void *ws, size_t ws_bytes, hipStream_t stream) {
+  const size_t need = moe_mlp_workspace_bytes(m.hidden, m.inter, m.halves, m.n);
+  if (need == 0 || ws_bytes < need) return hipErrorInvalidValue;
+  char *w = static_cast<char *>(ws);
+  const size_t act_bytes = m.n > 0 ? align256((size_t)m.n * m.inter * 2) : 0;
+  uint16_t *act = m.act ? m.act : reinterpret_cast<uint16_t *>(w + kWsReserved);
+  float *partials = reinterpret_cast<float *>(w + kWsReserved + act_bytes);
+  const size_t room = ws_bytes - kWsReserved - act_bytes;
+  if (m.n > 0) {
+    const hipError_t e = launch_list(mlp_gate_up(m, act), w, partials, room, stream);
+    if (e != hipSuccess) return e;
+  }
+  const GemvLaunch d = mlp_down(m, act);
+  if (m.n <= 0) return launch_gemv(d, ws, ws_bytes, stream);
+  return launch_list(d, w, partials, room, stream);
 }
 
 }  // namespace trellis

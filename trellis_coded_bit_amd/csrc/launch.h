@@ -22,7 +22,25 @@ hipError_t launch_had128(const void *x, int x_is_fp32, int rows, int n, const ui
                          const float *s, int post, float norm, void *y, int y_is_fp32,
                          hipStream_t stream);
 
-// How the finishing launch combines the column blocks of a GEMV problem list.
+// Every workspace starts with the same reserved region, so that one zero-filled buffer can
+// serve every entry point in any order:
+//   [0, 256)                 header; word 0 is the error word (sticky: kernels only OR bits
+//                            into it, the caller clears it); words 16-17 the small-batch
+//                            products' chunk queue (zero between calls)
+//   [256, 256 + 64 KiB)      the small-batch products' column-block counters: zero between
+//                            calls (each call's finishing workgroups reset the ones it used);
+//                            no other entry point writes them
+//   [kWsReserved, ...)       the entry point's own scratch
+constexpr size_t kWsHeaderBytes = 256;
+constexpr size_t kWsQueueOffset = 64;  // header words 16, 17: the small-batch chunk queue (zero between calls)
+constexpr int kMaxFinishGroups = 16384;
+constexpr size_t kWsCounterBytes = (size_t)kMaxFinishGroups * 4;
+constexpr size_t kWsReserved = kWsHeaderBytes + kWsCounterBytes;
+// Error-word bits.
+constexpr uint32_t kErrBadEntry = 1u;    // a routed id out of range or a table entry with bad K / cb
+constexpr uint32_t kErrWaitExpired = 2u; // a bounded wait for another workgroup ran out (prefill)
+
+// How the small-batch products finish a column block.
 enum GemvFinish {
   kFinishPlain = 0,     // y[p] = had(y_pre[p]) * sv_p for every problem p
   kFinishSwiGLU = 1,    // problems in slots of 2H (H gate entries, then H up entries):
@@ -30,32 +48,45 @@ enum GemvFinish {
   kFinishWeighted = 2,  // y = had(sum_p w[p] * y_pre[p]) * sv, sv shared   (B = 1)
 };
 
-// One product problem list: either a single layer (table == NULL) or the routed entries of
-// a device table.  With `group` entries per expert, problem p uses table entry
-// routed[p / group] * group + p % group.
+// One layer of a list-mode launch: its descriptor and its own input and output.
+constexpr int kMaxList = 8;
+struct GemvItem {
+  trellis_linear L;
+  const uint16_t *x;  // fp16 [B][L.in_features]
+  uint16_t *y;        // fp16 [B][L.out_features]
+};
+
+// One product problem list, in one of two modes:
+//   list mode  (table == NULL): n_list layers of any shapes, each with its own x and y;
+//   table mode (table != NULL): the routed entries of a device table, all [in, out]; with
+//     `group` entries per expert, problem p uses entry routed[p / group] * group + p % group.
 struct GemvLaunch {
-  trellis_linear single;         // used when table == NULL
+  int n_list;
+  GemvItem list[kMaxList];
   const trellis_linear *table;   // device table [E * group] or NULL
   int E;                         // experts (valid routed ids are 0..E-1)
   int group;                     // table entries per expert (>= 1)
   const int32_t *routed;         // device [n_problems / group] (table mode)
-  int n_problems;
-  int in_features, out_features, B;
-  const uint16_t *x;
+  int n_problems;                // table mode
+  int in_features, out_features; // table mode
+  int B;
+  const uint16_t *x;             // table mode
   int x_per_problem;
-  uint16_t *y;
+  uint16_t *y;                   // table mode
   const uint16_t *shared_r;
   const float *shared_s;
   int shared_side;
-  int finish;                    // GemvFinish
+  int finish;                    // GemvFinish (table mode; list mode is always plain)
   int halves;                    // kFinishSwiGLU: H
   const float *router_w;         // kFinishWeighted: device f32 [n_problems]
 };
 
-// Workspace bytes for a GEMV launch with n_problems problems of [in, out] at batch B.
+// Workspace bytes of a launch (including the reserved region); 0 if it is not supported
+// (more column blocks than the counter region holds, or too many units).
+size_t gemv_workspace_bytes(const GemvLaunch &a);
+// The same for a table-mode launch of n_problems [in, out] problems at batch B.
 size_t gemv_workspace_bytes(int n_problems, int in_features, int out_features, int B);
-// Upper bound on n_problems * out_features / 128 for one GEMV/MoE call.
-int gemv_max_column_blocks();
+// The launch: one kernel (plus nothing else), or a zero fill for an empty weighted sum.
 hipError_t launch_gemv(const GemvLaunch &a, void *ws, size_t ws_bytes, hipStream_t stream);
 
 // Routed-expert MLP of one token: gate/up halves (table [E][2H]) -> silu(g)*u -> down
@@ -87,5 +118,13 @@ hipError_t launch_gemm(const trellis_linear &L, const uint16_t *x, int M, uint16
 size_t gemm_fp8_workspace_bytes(int in_features, int out_features, int M);
 hipError_t launch_gemm_fp8(const trellis_linear &L, const uint16_t *x, int M, uint16_t *y, void *ws,
                            size_t ws_bytes, hipStream_t stream);
+
+// Microbenchmarks (include/trellis_micro.h).
+int micro_cus();
+hipError_t launch_micro_stream_read(const void *buf, size_t bytes, int blocks, uint32_t *sink, hipStream_t stream);
+hipError_t launch_micro_valu(int op, int iters, int waves_per_simd, uint64_t *cycles, uint64_t *ticks, uint32_t *sink,
+                             hipStream_t stream, int *blocks_out);
+hipError_t launch_micro_mfma(int kind, int iters, int waves_per_simd, uint64_t *cycles, uint64_t *ticks, float *sink,
+                             hipStream_t stream, int *blocks_out);
 
 }  // namespace trellis

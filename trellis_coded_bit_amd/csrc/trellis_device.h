@@ -115,6 +115,18 @@ __device__ __forceinline__ T ldg(const T *p) {
   return *(const __attribute__((address_space(1))) T *)p;
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (loads past the end return zero, stores
+// past it are dropped).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, long long bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
+// Cache-policy operand of the buffer intrinsics: SC1, device (agent) scope.  Data that one
+// workgroup stores and another (possibly on another XCD, with its own L2) reads after a
+// device-scope atomic is written and read with it.
+constexpr int kSC1 = 16;
+
 __device__ __forceinline__ float h2f(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
@@ -148,6 +160,15 @@ __device__ __forceinline__ void fwht_stage(float &a, float &b, int lane) {
   const float sg = (lane & M) ? -1.f : 1.f;
   a = lane_xor<M>(a) + sg * a;
   b = lane_xor<M>(b) + sg * b;
+}
+
+// The four butterfly stages across the 16 lanes of a row (strides 1, 2, 4, 8), for values
+// held one per lane and row.
+__device__ __forceinline__ void fwht_stage1(float &v, int lane) {
+  v = lane_xor<1>(v) + ((lane & 1) ? -v : v);
+  v = lane_xor<2>(v) + ((lane & 2) ? -v : v);
+  v = lane_xor<4>(v) + ((lane & 4) ? -v : v);
+  v = lane_xor<8>(v) + ((lane & 8) ? -v : v);
 }
 
 // Unnormalised Sylvester Hadamard butterfly over 128 values held two per lane: element
