@@ -156,6 +156,17 @@ size_t trellis_gemv_list_workspace_bytes(const trellis_gemv_item *items, int n, 
 
 int trellis_gemv_list(const trellis_gemv_item *items, int n, int B, void *ws, size_t ws_bytes, void *stream);
 
+/* trellis_gemv_list without a workspace argument, for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * kernels and results, with the scratch (counters and partial sums) in a buffer of 32 MiB
+ * that the library holds in device memory, one per device, for the life of the process.
+ * Allocates nothing and calls no allocating routine.  Every call on a device shares that
+ * device's buffer, so calls that overlap in time on one device (several streams or threads)
+ * race and must not be made.  A request needing more scratch than the buffer holds is
+ * rejected with TRELLIS_EUNSUPPORTED before anything is enqueued (a dense MLP step of three
+ * 5120 <-> 17408 matrices needs about 1 MiB of it at batch 1, 8 MiB at batch 8). */
+int trellis_gemv_list_noalloc(const trellis_gemv_item *items, int n, int B, void *stream);
+
 /* Prefill product, same definition as trellis_gemv for M rows (M >= 1).
  * x: fp16 [M][in], y: fp16 out [M][out].
  * ws: zero-filled device workspace of >= trellis_workspace_bytes(GEMM, L, M, 0) bytes

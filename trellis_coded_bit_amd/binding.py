@@ -103,6 +103,8 @@ def lib() -> ctypes.CDLL:
             L.trellis_gemv_list_workspace_bytes.argtypes = [vp, i32, i32]
             L.trellis_gemv_list.restype = i32
             L.trellis_gemv_list.argtypes = [vp, i32, i32, vp, sz, vp]
+            L.trellis_gemv_list_noalloc.restype = i32
+            L.trellis_gemv_list_noalloc.argtypes = [vp, i32, i32, vp]
             L.trellis_validate_table.restype = i32
             L.trellis_validate_table.argtypes = [ctypes.POINTER(CLinear), i32, i32, i32, i32]
             _lib = L

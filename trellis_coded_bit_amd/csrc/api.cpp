@@ -209,6 +209,25 @@ int trellis_gemv_list(const trellis_gemv_item *items, int n, int B, void *ws, si
   return hip_status(trellis::launch_gemv(a, ws, ws_bytes, as_stream(stream)), "trellis_gemv launch");
 }
 
+int trellis_gemv_list_noalloc(const trellis_gemv_item *items, int n, int B, void *stream) {
+  g_err[0] = 0;
+  trellis::GemvLaunch a;
+  int st = make_list_launch(items, n, B, &a);
+  if (st) return st;
+  const size_t need = trellis::gemv_workspace_bytes(a);
+  if (need == 0)
+    return fail(TRELLIS_EUNSUPPORTED, "more than %d output column blocks or 2^31 units in one call",
+                trellis::kMaxFinishGroups);
+  if (need > trellis::kNoAllocScratchBytes)
+    return fail(TRELLIS_EUNSUPPORTED, "this call needs %zu bytes of scratch; the allocation-free entry point holds %zu",
+                need, trellis::kNoAllocScratchBytes);
+  void *ws = nullptr;
+  st = hip_status(trellis::noalloc_scratch(&ws), "trellis_gemv_list_noalloc scratch lookup");
+  if (st) return st;
+  return hip_status(trellis::launch_gemv(a, ws, trellis::kNoAllocScratchBytes, as_stream(stream)),
+                    "trellis_gemv_list_noalloc launch");
+}
+
 int trellis_gemm(const trellis_linear *L, const uint16_t *x, int M, uint16_t *y, void *ws,
                  size_t ws_bytes, void *stream) {
   g_err[0] = 0;

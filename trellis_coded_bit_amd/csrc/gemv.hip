@@ -46,6 +46,7 @@
 // (2^-4 is exact; the output side applies 2^-7 / 2^-4 = 2^-3).
 #include <climits>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "launch.h"
@@ -1137,6 +1138,34 @@ size_t gemv_workspace_bytes(int n_problems, int in_features, int out_features, i
   a.out_features = out_features;
   a.B = B;
   return gemv_workspace_bytes(a);
+}
+
+// Scratch of the allocation-free entry point: a workspace (reserved region, then partials)
+// in device memory that the library itself holds, one copy per device, zero at load and
+// left with zero counters by every call.  In host code `scratch` is only a stand-in for the
+// symbol: its device address is looked up once per device and kept in g_scratch_ptr.
+__device__ __attribute__((aligned(256))) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t noalloc_scratch(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // (the current device's copy)
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_gemv(const GemvLaunch &a, void *ws, size_t ws_bytes, hipStream_t stream) {

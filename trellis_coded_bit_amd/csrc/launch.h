@@ -88,6 +88,9 @@ size_t gemv_workspace_bytes(const GemvLaunch &a);
 size_t gemv_workspace_bytes(int n_problems, int in_features, int out_features, int B);
 // The launch: one kernel (plus nothing else), or a zero fill for an empty weighted sum.
 hipError_t launch_gemv(const GemvLaunch &a, void *ws, size_t ws_bytes, hipStream_t stream);
+// The library-held scratch of the allocation-free entry point (the current device's copy).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void **ptr);
 
 // Routed-expert MLP of one token: gate/up halves (table [E][2H]) -> silu(g)*u -> down
 // (table [E]) -> router-weighted sum with one output rotation.
