@@ -270,3 +270,27 @@ def test_encode_validation(L):
     assert call(t=None) == EINVAL and call(code=None) == EINVAL
     assert call(t=0x10002) == EALIGN and call(code=0x20002) == EALIGN and call(st=0x30001) == EALIGN
     assert call(nb=need - 1) == EWORKSPACE and call(ws=None) == EWORKSPACE and call(ws=0x100010) == EWORKSPACE
+
+
+def test_abi_layer_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """csrc/api.cpp (the C-ABI layer: validation, error strings, marshalling) built with the
+    host compiler under AddressSanitizer and UndefinedBehaviorSanitizer, warnings as errors,
+    against stub launchers (tests/sanitize/abi_driver.cpp), and every entry point called
+    with good and bad arguments: no sanitizer report, every expectation met."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no host C++ compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = str(tmp_path / "abi_driver")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-Wall", "-Wextra", "-Werror", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           os.path.join(root, "trellis_coded_bit_amd", "csrc", "api.cpp"),
+           os.path.join(root, "tests", "sanitize", "abi_driver.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "failures 0" in r.stdout

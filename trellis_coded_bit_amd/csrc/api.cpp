@@ -1,6 +1,6 @@
 // C ABI of libtrellis.so: argument validation, error reporting and dispatch to the gfx950
 // launchers.  The contract (meaning, layout, ownership, errors) is in include/trellis.h.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cstdarg>
 #include <cstdio>
@@ -151,7 +151,7 @@ int make_list_launch(const trellis_gemv_item *items, int n, int B, trellis::Gemv
     int st = check_linear(&it.L, 1);
     if (st) {
       char tmp[512];
-      snprintf(tmp, sizeof(tmp), "item %d: %s", p, g_err);
+      snprintf(tmp, sizeof(tmp), "item %d: %.480s", p, g_err);
       snprintf(g_err, sizeof(g_err), "%s", tmp);
       return st;
     }
@@ -403,7 +403,7 @@ int trellis_validate_table(const trellis_linear *host_table, int E, int in_featu
     int st = check_linear(&c, 1);
     if (st) {
       char tmp[512];
-      snprintf(tmp, sizeof(tmp), "entry %d: %s", e, g_err);
+      snprintf(tmp, sizeof(tmp), "entry %d: %.480s", e, g_err);
       snprintf(g_err, sizeof(g_err), "%s", tmp);
       return st;
     }

@@ -1,7 +1,7 @@
 // Internal launchers behind the C ABI (see include/trellis.h for the public contract).
 // Arguments here are already validated by api.cpp.
 #pragma once
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
