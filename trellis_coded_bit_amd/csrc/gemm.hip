@@ -436,20 +436,25 @@ __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][
   // are loaded two steps ahead (past the piece they fetch unused data).
   // The previous piece's output stores must have completed first: with stores and loads
   // both outstanding the compiler can no longer count loads in order and would wait for
-  // all of them inside the loop.  The prologue issues its loads in the loop's own order.
+  // all of them inside the loop.  The loads left outstanding when the loop starts are
+  // issued in the order one iteration leaves them (codes s+2, activations s, codes s+3,
+  // activations s+1): the compiler counts outstanding loads per instruction position and
+  // takes, at the loop head, the stricter of the entry and the back edge, so any other
+  // order would make each iteration wait for loads issued only just before.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   load_c(CR0, s0);
+  load_c(CR1, s0 + 1);
+  stage_c(CR0, 0);
+  stage_c(CR1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_c(CR0, s0 + 2);
   __builtin_amdgcn_sched_barrier(0);
   load_a(A0, s0);
   __builtin_amdgcn_sched_barrier(0);
-  load_c(CR1, s0 + 1);
+  load_c(CR1, s0 + 3);
   __builtin_amdgcn_sched_barrier(0);
   load_a(A1, s0 + 1);
   __builtin_amdgcn_sched_barrier(0);
-  stage_c(CR0, 0);
-  load_c(CR0, s0 + 2);
-  stage_c(CR1, 1);
-  load_c(CR1, s0 + 3);
   decode_to(0, 0);
   lds_barrier();
   // Every thread passed vmcnt(0) above, so partial-tile stores issued before this piece
@@ -479,6 +484,9 @@ __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][
     read_b(1, 0);
     mfma_half(A0, 4);
     load_a(A0, s + 2);
+    // (keeps the next step's MFMAs out of this group: hoisted here they would wait on
+    // activations loaded only half a step earlier)
+    __builtin_amdgcn_sched_barrier(0);
     // step s + 1 (B slot 1)
     mfma_half(A1, 0);
     read_b(1, 4);
@@ -490,6 +498,11 @@ __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][
     read_b(0, 0);               // step s + 2 (unused after the last pair)
     mfma_half(A1, 4);
     load_a(A1, s + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    // Keeps these B reads in this iteration: with nothing that may write memory after
+    // them, the compiler would merge them with the prologue's identical reads into one
+    // read at the top of the loop, right before the MFMAs that wait for it.
+    asm volatile("" ::: "memory");
   }
   lds_barrier();  // the rings' last reads are done before the next piece writes them
 }
