@@ -455,32 +455,38 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((address_space(3))) void *lds_void_ptr;
 
-// Copy the wave's two tile rows of the unit whose rows start at `row0` (global words) into
-// ring slot `dst` (LDS).  `real` = false: every lane reads the first 16 bytes of `row0`.
+// Copy the wave's two tile rows of a unit into ring slot `dst` (LDS).  The copies are
+// buffer loads straight into LDS over the problem's code array (scalar resource `rc`):
+// `off` (bytes, wave-uniform) is where the unit's first row starts, `rs` the row stride in
+// words.  `real` = false: a dummy copy of the array's first bytes (the count of copies per
+// unit stays fixed).  Every offset is 32-bit (a problem's code array is under 2 GiB), so no
+// per-lane 64-bit address is kept live across the loop.
 template <int K>
-__device__ __forceinline__ void dma_unit(const uint32_t *row0, size_t row_stride_words, uint32_t *dst, bool real) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void dma_unit(__amdgpu_buffer_rsrc_t rc, uint32_t off, uint32_t rs, uint32_t *dst,
+                                         bool real) {
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // (recomputed here: cheaper than keeping it live)
+  const uint32_t so = real ? off : 0u;
   if constexpr (K == 2) {
     // 2 x 512 B: lanes 0..31 take row 0, lanes 32..63 row 1, 16 B each
-    const uint32_t *src = row0 + (real ? ((size_t)(lane >> 5) * row_stride_words + 4 * (lane & 31)) : 0);
-    __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_ptr)dst, 16, 0, 0);
+    const uint32_t vo = 4u * ((uint32_t)(lane >> 5) * rs + 4u * (uint32_t)(lane & 31));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void_ptr)dst, 16, vo, so, 0, 0);
   } else if constexpr (K == 3) {
     // 2 x 768 B = 96 pieces of 16 B: lanes 0..63 take pieces 0..63, then lanes 0..31 take
     // pieces 64..95 (a piece never straddles the two rows: 768 is a multiple of 16)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int piece = 64 * c + lane;
-      const int r = piece / 48, w = 4 * (piece - 48 * r);
-      const uint32_t *src = row0 + (real ? ((size_t)r * row_stride_words + w) : 0);
-      if (c == 0 || lane < 32)
-        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_ptr)(dst + c * 256), 16, 0, 0);
+      const int r = piece >= 48 ? (piece >= 96 ? 2 : 1) : 0;
+      const uint32_t vo = 4u * ((uint32_t)r * rs + 4u * (uint32_t)(piece - 48 * r));
+      if (c == 0 || lane < 32) __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void_ptr)(dst + c * 256), 16, vo, so, 0, 0);
     }
   } else {
     // 2 x 1024 B: one copy per row, 16 B per lane
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const uint32_t *src = row0 + (real ? ((size_t)r * row_stride_words + 4 * lane) : 0);
-      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_ptr)(dst + r * 256), 16, 0, 0);
+      const uint32_t vo = 4u * ((uint32_t)r * rs + 4u * (uint32_t)lane);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void_ptr)(dst + r * 256), 16, vo, so, 0, 0);
     }
   }
 }
@@ -510,8 +516,12 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
   const int mc = m < B ? m : B - 1;  // batch row of the A operand (rows past B are ignored)
   const uint32_t a_lane = (uint32_t)((grp * B + mc) << 2);
   const size_t row_stride = (size_t)Tj * NW;
-  const uint32_t *code = pr.code + (size_t)(2 * wave) * row_stride;
-  const size_t row_block_words = 8 * row_stride;
+  // the problem's code array as a buffer; offsets in bytes from its start (32-bit: arrays
+  // of 2 GiB or more are rejected at launch)
+  const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(pr.code, (long long)(pr.in / 16) * (long long)row_stride * 4);
+  const uint32_t rs = (uint32_t)row_stride;
+  const uint32_t code_off = (uint32_t)(2 * wave) * rs * 4u;  // this wave's two tile rows
+  const uint32_t row_block_bytes = 8u * rs * 4u;
   const int first = __builtin_amdgcn_readfirstlane(ub - units_base<LIST>(P, p));
   const int total = __builtin_amdgcn_readfirstlane(ue - ub);
   const int in = pr.in;
@@ -522,7 +532,7 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
   // sub-range bookkeeping, lane constants): its address needs only the first unit's (I, J).
   if (fresh) {
     const int I0 = __builtin_amdgcn_readfirstlane(first % nI), J0 = __builtin_amdgcn_readfirstlane(first / nI);
-    dma_unit<K>(code + (size_t)I0 * row_block_words + (size_t)(8 * J0) * NW, row_stride, ring, true);
+    dma_unit<K>(rc, code_off + (uint32_t)I0 * row_block_bytes + (uint32_t)(8 * J0 * NW * 4), rs, ring, true);
     __builtin_amdgcn_sched_barrier(0);
   }
   floatx4 acc[8];
@@ -545,14 +555,14 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
     int pre_I = cur_I;
     // next unit to request: its rows start at nxt (uniform); one step along I adds a row
     // block, the wrap to the next column block moves 8 tiles right and back to I = 0
-    const uint32_t *nxt = code + (size_t)pre_I * row_block_words + (size_t)(8 * cur_J) * NW;
-    const size_t wrap_back = (size_t)(nI - 1) * row_block_words;
+    uint32_t nxt = code_off + (uint32_t)pre_I * row_block_bytes + (uint32_t)(8 * cur_J * NW * 4);
+    const uint32_t wrap_back = (uint32_t)(nI - 1) * row_block_bytes;
     auto advance = [&]() {
       if (++pre_I == nI) {
         pre_I = 0;
-        nxt = nxt - wrap_back + 8 * NW;
+        nxt = nxt - wrap_back + 8u * NW * 4u;
       } else {
-        nxt += row_block_words;
+        nxt += row_block_bytes;
       }
     };
     // the previous sub-range's reads of the A buffer and of the ring are finished (nothing
@@ -564,7 +574,7 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
     // deeper prefetches, so the decode starts sooner.
     auto prime = [&](int j) {
       const bool real = j < n;
-      dma_unit<K>(real ? nxt : code, row_stride, ring + j * (RG::UNIT_BYTES / 4), real);
+      dma_unit<K>(rc, nxt, rs, ring + j * (RG::UNIT_BYTES / 4), real);
       if (real) advance();
     };
     if (fresh && sb == 0) advance();  // (its copy was issued above)
@@ -616,7 +626,7 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
       {
         const int ws = (slot == 0 ? SLOTS : slot) - 1;
         const bool real = k + SLOTS - 1 < n;
-        dma_unit<K>(real ? nxt : code, row_stride, ring + ws * (RG::UNIT_BYTES / 4), real);
+        dma_unit<K>(rc, nxt, rs, ring + ws * (RG::UNIT_BYTES / 4), real);
         if (real) advance();
       }
       wait_vmcnt<RG::WAIT>();  // unit k has landed
@@ -1013,6 +1023,17 @@ Geometry geometry(const GemvLaunch &a) {
     nI_min = nI;
   }
   if (U <= 0 || U >= (1LL << 31) || nq > kMaxFinishGroups) return gm;
+  // code offsets are 32-bit byte offsets from each array's start: every code array is
+  // under 2 GiB (in * out * K / 8 bytes, K <= 4)
+  {
+    const long long max_code = 1LL << 31;
+    if (a.table == nullptr) {
+      for (int p = 0; p < a.n_list; ++p)
+        if ((long long)a.list[p].L.in_features * a.list[p].L.out_features / 2 >= max_code) return gm;
+    } else if ((long long)a.in_features * a.out_features / 2 >= max_code) {
+      return gm;
+    }
+  }
   gm.U = (int)U;
   gm.nq = (int)nq;
   gm.nf = a.table && a.finish == kFinishSwiGLU ? gm.nq / 2
