@@ -494,8 +494,8 @@ __device__ __forceinline__ void dma_unit(__amdgpu_buffer_rsrc_t rc, uint32_t off
 // Units [ub, ue) of problem p (width K), part of chunk c, in sub-ranges of at most P.kA
 // units.  Each sub-range issues its rotation loads and its first code copies, rotates while
 // the code is in flight, then streams with SLOTS - 1 units in flight per wave.  q0: the
-// chunk's first column block (segment numbering).  fresh: the workgroup's first part (its
-// first code copy was issued before the set-up).
+// chunk's first column block (segment numbering).  fresh: the workgroup's first part
+// (nothing of an earlier part to wait for).
 // CB = 2 (the E4M3 codebook, "EXLR8" page): each lane's four values are the E4M3-rounded
 // codebook values, converted back to fp16 (exact) and fed to v_mfma_f32_16x16x16_f16 with
 // the A operand's duplicated words repacked once per tile row into (x0, x1), (x8, x9).
@@ -528,13 +528,6 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
   const uint16_t *xp = pr.x;
   const int qp = __builtin_amdgcn_readfirstlane(blocks_base<LIST>(P, p) - q0);  // segment of J = 0
 
-  // The workgroup's first copy goes out before the rest of the set-up (priority thresholds,
-  // sub-range bookkeeping, lane constants): its address needs only the first unit's (I, J).
-  if (fresh) {
-    const int I0 = __builtin_amdgcn_readfirstlane(first % nI), J0 = __builtin_amdgcn_readfirstlane(first / nI);
-    dma_unit<K>(rc, code_off + (uint32_t)I0 * row_block_bytes + (uint32_t)(8 * J0 * NW * 4), rs, ring, true);
-    __builtin_amdgcn_sched_barrier(0);
-  }
   floatx4 acc[8];
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -568,18 +561,24 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
     // the previous sub-range's reads of the A buffer and of the ring are finished (nothing
     // to wait for on the workgroup's first sub-range)
     if (!(fresh && sb == 0)) __syncthreads();
-    // The first unit into slot 0, then the rotation's loads; units 1..SLOTS-2 are requested
-    // after the rotation.  At the start of the kernel every wave requests code at once: asking for
-    // one unit each first lets the memory system serve everybody's first unit before the
-    // deeper prefetches, so the decode starts sooner.
+    // The rotation's loads, then the first unit into slot 0; units 1..SLOTS-2 are requested
+    // after the rotation.  Vector memory operations complete in issue order, so loads issued
+    // after a code copy would wait for it: issued first, the (cache-resident) activations
+    // and side vectors arrive while the copy is in flight and the rotation runs under it.
+    // At the start of the kernel every wave requests code at once: asking for one unit each
+    // first lets the memory system serve everybody's first unit before the deeper
+    // prefetches, so the decode starts sooner.
     auto prime = [&](int j) {
       const bool real = j < n;
       dma_unit<K>(rc, nxt, rs, ring + j * (RG::UNIT_BYTES / 4), real);
       if (real) advance();
     };
-    if (fresh && sb == 0) advance();  // (its copy was issued above)
-    else prime(0);
-    if (sb == 0) set_priority(prio_at(ub));  // (after the first copy is on its way)
+    auto first_copy = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      prime(0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (sb == 0) set_priority(prio_at(ub));  // (after the first copy is on its way)
+    };
     // Rotation loads: straight-line code (tasks past the last are clamped to it and their
     // values ignored), so all of them are in flight together.
     const bool vec = ((reinterpret_cast<uintptr_t>(xp) | reinterpret_cast<uintptr_t>(pr.rin) |
@@ -589,6 +588,7 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
       const int I = (first + sb + task / B) % nI;
       const RotVec q = pr.s_in ? rot_vec_load<true>(xp, pr.rin, pr.s_in, in, B, task, I)
                                : rot_vec_load<false>(xp, pr.rin, pr.s_in, in, B, task, I);
+      first_copy();
       rot_vec_compute(B, n, wave + kWaves * (lane >> 4), q, sm);
     } else {
     RotLoads rq;
@@ -614,6 +614,7 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
     };
     if (pr.s_in) load_tasks(std::true_type{});
     else load_tasks(std::false_type{});
+    first_copy();
     rotation_compute(B, n, wave, rq, sm);
     }
     __syncthreads();  // (also waits for unit 0)
@@ -755,6 +756,48 @@ __device__ void finish_plain(const GemvParams &P, const Lds &sm, int q) {
   __syncthreads();
 }
 
+// Batch 1: two plain finishes at once, waves 0-1 finishing column block qa and waves 2-3
+// block qb (qb < 0: none).  A block's 128 sums need only half the workgroup, and a
+// workgroup that arrives last at two blocks would otherwise pay the partials' load latency
+// twice.  The partials are added in chunk order, as finish_plain adds them.
+template <bool LIST>
+__device__ void finish_plain_pair(const GemvParams &P, const Lds &sm, int qa, int qb) {
+  const int tid = threadIdx.x, h = tid >> 7, t = tid & 127, lane = tid & 63;
+  const int q = __builtin_amdgcn_readfirstlane(h ? qb : qa);
+  float v = 0.f;
+  if (q >= 0) {
+    const BlockChunks c = block_chunks<LIST>(P, q);
+    const __amdgpu_buffer_rsrc_t rp = buffer_rsrc(P.partials, P.partial_bytes);
+    constexpr int kBatch = 16;
+    for (int gb = c.lo; gb <= c.hi; gb += kBatch) {
+      float part[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int gg = gb + k;
+        const uint32_t slot = (uint32_t)(gg * P.maxseg + (gg == c.lo ? c.seg_lo : 0));
+        part[k] = gg <= c.hi ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, (slot * 128 + t) * 4, 0, kSC1))
+                             : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) v += part[k];
+    }
+  }
+  sm.red[h * 128 + t] = v;
+  __syncthreads();
+  if (q >= 0 && ((tid >> 6) & 1) == 0) {
+    const int p = problem_of_block<LIST>(P, q), J = q - blocks_base<LIST>(P, p);
+    const Problem pr = get_problem<LIST>(P, p);
+    float2 sc = {0.f, 0.f};
+    if (pr.ok) sc = out_scales(pr.rout, pr.s_out, J, lane);
+    float va = sm.red[h * 128 + lane], vb = sm.red[h * 128 + lane + 64];
+    wave_fwht128(va, vb);
+    const int c0 = J * 128 + lane;
+    pr.y[c0] = f2h(va * sc.x);  // (an invalid problem has zero scales)
+    pr.y[c0 + 64] = f2h(vb * sc.y);
+  }
+  __syncthreads();
+}
+
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z) ("EXLR8" page, calibration paragraph: the
 // expert's down projection reads silu(gate x) * up x).  For z below about -88 e^-z is
 // +inf in fp32 and the quotient is -0, the limit.
@@ -877,16 +920,39 @@ __device__ void arrive_chunk(const GemvParams &P, const Lds &sm, int c, int *nex
     if (base == q0 && threadIdx.x == kThreads - 1) *next = P.n_chunks > P.G ? (int)got + P.G : P.n_chunks;
     __syncthreads();
     const int cnt = min(kThreads, q1 - base + 1);
-    for (int i = 0; i < cnt; ++i) {
-      if (__builtin_amdgcn_readfirstlane(flags[i])) {
-        const int f = group_of_block<LIST>(P, base + i);
-        // The other chunks' partials are read after their arrivals were seen, with
-        // device-scope (sc1) loads, which read the coherent copy (the per-XCD L2s hold no
-        // stale one): no cache invalidation is needed.
-        if (LIST || P.L.finish == kFinishPlain) finish_plain<LIST>(P, sm, f);
-        else if (P.L.finish == kFinishSwiGLU) finish_swiglu(P, sm, f);
-        else finish_weighted(P, sm, f);
-        if (threadIdx.x == 0) __hip_atomic_store(P.counters + f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The other chunks' partials are read after their arrivals were seen, with device-scope
+    // (sc1) loads, which read the coherent copy (the per-XCD L2s hold no stale one): no
+    // cache invalidation is needed.
+    if (LIST && P.L.B == 1) {
+      int pend = -1;  // (uniform)
+      for (int i = 0; i < cnt; ++i) {
+        if (__builtin_amdgcn_readfirstlane(flags[i])) {
+          const int f = group_of_block<LIST>(P, base + i);
+          if (pend < 0) {
+            pend = f;
+            continue;
+          }
+          finish_plain_pair<LIST>(P, sm, pend, f);
+          if (threadIdx.x == 0) {
+            __hip_atomic_store(P.counters + pend, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(P.counters + f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          pend = -1;
+        }
+      }
+      if (pend >= 0) {
+        finish_plain_pair<LIST>(P, sm, pend, -1);
+        if (threadIdx.x == 0) __hip_atomic_store(P.counters + pend, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      for (int i = 0; i < cnt; ++i) {
+        if (__builtin_amdgcn_readfirstlane(flags[i])) {
+          const int f = group_of_block<LIST>(P, base + i);
+          if (LIST || P.L.finish == kFinishPlain) finish_plain<LIST>(P, sm, f);
+          else if (P.L.finish == kFinishSwiGLU) finish_swiglu(P, sm, f);
+          else finish_weighted(P, sm, f);
+          if (threadIdx.x == 0) __hip_atomic_store(P.counters + f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
     __syncthreads();
