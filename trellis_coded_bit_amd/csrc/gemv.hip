@@ -297,7 +297,7 @@ struct RotLoads {
 };
 
 __device__ __forceinline__ void rotation_compute(int B, int n, int wave, const RotLoads &rl, const Lds &sm) {
-  const int lane = threadIdx.x & 63;
+  const int lane = opaque_tid() & 63;
 #pragma unroll
   for (int t = 0; t < kMaxTasks; ++t) {
     const int task = wave + kWaves * t;
@@ -331,7 +331,7 @@ struct RotVec {
 template <bool WITH_S>
 __device__ __forceinline__ RotVec rot_vec_load(const uint16_t *xp, const uint16_t *rin, const float *s_in, int in,
                                                int B, int task, int I) {
-  const int i = threadIdx.x & 15;
+  const int i = opaque_tid() & 15;
   const int s = task / B, b = task - s * B;
   (void)s;
   const int k = I * 128 + 8 * i;
@@ -349,7 +349,7 @@ __device__ __forceinline__ RotVec rot_vec_load(const uint16_t *xp, const uint16_
 }
 
 __device__ __forceinline__ void rot_vec_compute(int B, int n, int task, const RotVec &q, const Lds &sm) {
-  const int lane = threadIdx.x & 63, i = lane & 15;
+  const int lane = opaque_tid() & 63, i = lane & 15;
   float v[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -401,7 +401,7 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ void publish_partial(const GemvParams &P, const Lds &sm, int c, int seg,
                                                 floatx4 (&acc)[8]) {
   const int B = P.L.B;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int mrow = 4 * (lane >> 4) + r;
@@ -508,7 +508,11 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
   const int B = P.L.B;
   const int Tj = pr.out / 16;
   const int nI = pr.in / 128;
-  const int lane = threadIdx.x & 63;
+  // The lane's constants are derived here, per call: left to itself the compiler computes
+  // them once per width at kernel entry and keeps every width's set live across the chunk
+  // loop, which spills in the kernels that handle several widths.
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, grp = lane >> 4;
   const LaneWindow lw = lane_window(lane, K);
@@ -733,7 +737,7 @@ __device__ __forceinline__ float2 out_scales(const uint16_t *rout, const float *
 template <bool LIST>
 __device__ void finish_plain(const GemvParams &P, const Lds &sm, int q) {
   const int B = P.L.B;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int p = problem_of_block<LIST>(P, q), J = q - blocks_base<LIST>(P, p);
   const Problem pr = get_problem<LIST>(P, p);
   float2 sc = {0.f, 0.f};
@@ -762,7 +766,7 @@ __device__ void finish_plain(const GemvParams &P, const Lds &sm, int q) {
 // twice.  The partials are added in chunk order, as finish_plain adds them.
 template <bool LIST>
 __device__ void finish_plain_pair(const GemvParams &P, const Lds &sm, int qa, int qb) {
-  const int tid = threadIdx.x, h = tid >> 7, t = tid & 127, lane = tid & 63;
+  const int tid = opaque_tid(), h = tid >> 7, t = tid & 127, lane = tid & 63;
   const int q = __builtin_amdgcn_readfirstlane(h ? qb : qa);
   float v = 0.f;
   if (q >= 0) {
@@ -810,7 +814,7 @@ __device__ void finish_swiglu(const GemvParams &P, const Lds &sm, int f) {
   const int H = P.L.halves, nJ = P.nJ;
   const int slot = f / (H * nJ), rem = f - slot * H * nJ;
   const int pg = slot * 2 * H + rem / nJ, J = rem - (rem / nJ) * nJ;
-  const int tid = threadIdx.x, c = tid & 127, which = tid >> 7, lane = tid & 63;
+  const int tid = opaque_tid(), c = tid & 127, which = tid >> 7, lane = tid & 63;
   const int p = which ? pg + H : pg;
   const bool rot = (tid & 127) < 64;  // waves 0 (gate) and 2 (up)
   float2 sc = {0.f, 0.f};
@@ -855,7 +859,7 @@ __device__ void finish_swiglu(const GemvParams &P, const Lds &sm, int f) {
 // problem k's partials of block J) over k = r, r + 2, ..., in that order; the two sums are
 // added in r order, rotated once and scaled by the shared sv.
 __device__ void finish_weighted(const GemvParams &P, const Lds &sm, int J) {
-  const int tid = threadIdx.x, c = tid & 127, r = tid >> 7, lane = tid & 63;
+  const int tid = opaque_tid(), c = tid & 127, r = tid >> 7, lane = tid & 63;
   const int nJ = P.nJ, n = P.L.n_problems;
   const __amdgpu_buffer_rsrc_t rp = buffer_rsrc(P.partials, P.partial_bytes);
   float acc = 0.f;

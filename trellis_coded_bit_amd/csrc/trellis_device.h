@@ -108,6 +108,15 @@ __device__ __forceinline__ int lane_row(int lane, int j) {
   return 2 * (lane >> 4) + (j & 1) + 8 * (j >> 1);
 }
 
+// threadIdx.x, opaque to the optimiser: values derived from it are recomputed where they
+// are used instead of being hoisted to kernel entry and kept live across loops (in kernels
+// that inline several code paths the hoisted copies of every path's lane constants spill).
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Loads through the global address space (the pointers reach the kernels inside structs,
 // so the compiler cannot infer the address space and would otherwise emit flat loads).
 template <typename T>
@@ -177,7 +186,7 @@ __device__ __forceinline__ void fwht_stage1(float &v, int lane) {
 // seven 2x2 butterflies, so the stages may run in any order and the output uses the same
 // assignment as the input.
 __device__ __forceinline__ void wave_fwht128(float &a, float &b) {
-  const int lane = threadIdx.x & 63;
+  const int lane = opaque_tid() & 63;
   const float s = a + b, d = a - b;
   a = s;
   b = d;
