@@ -1065,6 +1065,7 @@ struct Geometry {
 // microseconds) at the end of the launch, where few workgroups remain to cover it.  The
 // default is therefore one equal static share per workgroup; the tail stays available.
 constexpr double kTailShare = 0.0;
+constexpr int kMinChunkAt4 = 13;
 constexpr int kSmallChunk = 2;
 constexpr int kMaxChunk = 32;
 
@@ -1109,7 +1110,12 @@ Geometry geometry(const GemvLaunch &a) {
   gm.nf = a.table && a.finish == kFinishSwiGLU ? gm.nq / 2
         : a.table && a.finish == kFinishWeighted ? a.out_features / 128 : gm.nq;
   int cus = 0;
-  const int occ = device_cus_and_occupancy(B, &cus);
+  int occ = device_cus_and_occupancy(B, &cus);
+  // Short chunks amortise a workgroup's set-up and finish latency poorly: with fewer than
+  // kMinChunkAt4 units each at four workgroups per CU, three per CU are used (measured on
+  // the MoE token, whose launches give 6-12 units per workgroup: 65.5 against 70-73 us;
+  // the dense MLP step, 16 units, is faster at four: 45.4 against 48.0 us).
+  if (occ >= 4 && U < (long long)kMinChunkAt4 * cus * occ) occ = 3;
   long long G = (long long)cus * occ;
   // Debug/test overrides of the workgroup count and the chunk size (they exercise chunks
   // that span column blocks and problems, and many chunks per workgroup).
