@@ -201,11 +201,10 @@ __device__ __forceinline__ u32x2 decode_pairs(uint32_t w0, uint32_t w1, uint32_t
   u32x2 out;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const uint32_t lo = __builtin_amdgcn_perm(h[2 * p + 1], h[2 * p], 0x05040100u);  // lo halves
-    const uint32_t hi = __builtin_amdgcn_perm(h[2 * p + 1], h[2 * p], 0x07060302u);  // hi halves
-    const half2_t v = __builtin_bit_cast(half2_t, lo) + __builtin_bit_cast(half2_t, hi);
-    out[p] = __builtin_bit_cast(uint32_t, v);
+    // one fp16 add of each word's halves (SDWA selects), value 2p low, 2p + 1 high
+    out[p] = mcg_value2(h[2 * p], h[2 * p + 1]);
     if constexpr (CB == 2) {
+      const half2_t v = __builtin_bit_cast(half2_t, out[p]);
       typedef short sv2 __attribute__((ext_vector_type(2)));
       const sv2 q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(sv2{0, 0}, v, 1.0f, false);
       out[p] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_bit_cast(uint32_t, q), 1.0f, false));

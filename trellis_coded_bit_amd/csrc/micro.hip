@@ -193,9 +193,14 @@ __global__ __launch_bounds__(kMicroThreads) void mfma_kernel(int iters, uint64_t
   if constexpr (KIND == TRELLIS_MICRO_MFMA_F16_16X16X32 || KIND == TRELLIS_MICRO_MFMA_F8_16X16X128) {
     floatx4 acc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, (float)j};
+    for (int j = 0; j < 8; ++j) {
+      // (a run-time start value: from constants the compiler builds the accumulators out of
+      // overlapping register ranges and copies them every iteration)
+      const float f = (float)(threadIdx.x + j);
+      acc[j] = floatx4{f, f, f, f};
+    }
     k0 = clocks_now();
-    for (int it = 0; it < iters; ++it)
+    for (int it = 0; it < iters; ++it) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if constexpr (KIND == TRELLIS_MICRO_MFMA_F16_16X16X32)
@@ -203,6 +208,10 @@ __global__ __launch_bounds__(kMicroThreads) void mfma_kernel(int iters, uint64_t
         else
           acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb, acc[j], 0, 0, 0, 0, 0, 0);
       }
+      // (keeps each accumulator in one accumulator-register range across iterations)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[j]));
+    }
     k1 = clocks_now();
 #pragma unroll
     for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][3];
