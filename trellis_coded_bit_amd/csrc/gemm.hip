@@ -398,10 +398,16 @@ __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][
   auto stage_c = [&](uint32_t c, int slot) {
     cw[slot * 2 * NW + cword] = c;  // repeated lanes store equal data
   };
-  auto decode_to = [&](int cslot, int slot) {
+  // The decode's window words are read from the code ring half a step before the decode
+  // (into W), so the decode does not start with an LDS round trip.
+  u32x4 W;
+  auto fetch_words = [&](int cslot) {
     const uint32_t *w = cw + cslot * 2 * NW;
-    const u32x2 t0 = decode_pairs<K, CB>(w[lw.d0], w[lw.d1], lw.sh);
-    const u32x2 t1 = decode_pairs<K, CB>(w[NW + lw.d0], w[NW + lw.d1], lw.sh);
+    W = u32x4{w[lw.d0], w[lw.d1], w[NW + lw.d0], w[NW + lw.d1]};
+  };
+  auto decode_to = [&](int slot) {
+    const u32x2 t0 = decode_pairs<K, CB>(W[0], W[1], lw.sh);
+    const u32x2 t1 = decode_pairs<K, CB>(W[2], W[3], lw.sh);
     ring[slot][wave][lane] = u32x4{t0[0], t0[1], t1[0], t1[1]};
   };
   // B operands of one step: column blocks 0..3 are read from the ring right after the
@@ -454,7 +460,9 @@ __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][
   __builtin_amdgcn_sched_barrier(0);
   load_a(A1, s0 + 1);
   __builtin_amdgcn_sched_barrier(0);
-  decode_to(0, 0);
+  fetch_words(0);
+  decode_to(0);
+  fetch_words(1);
   lds_barrier();
   // Every thread passed vmcnt(0) above, so partial-tile stores issued before this piece
   // have completed: publish them now (their latency was hidden behind the prologue).
@@ -477,8 +485,9 @@ __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][
     read_b(0, 4);
     stage_c(CR0, (r + 2) & 3);  // codes of step s + 2
     load_c(CR0, s + 4);
-    decode_to((r + 1) & 3, 1);  // step s + 1
+    decode_to(1);  // step s + 1 (words fetched half a step ago)
     interleave();
+    fetch_words((r + 2) & 3);  // step s + 2's words (staged above: same wave, in order)
     lds_barrier();
     read_b(1, 0);
     mfma_half(A0, 4);
@@ -491,8 +500,9 @@ __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][
     read_b(1, 4);
     stage_c(CR1, (r + 3) & 3);  // codes of step s + 3
     load_c(CR1, s + 5);
-    decode_to((r + 2) & 3, 0);  // step s + 2 (unused after the last pair)
+    decode_to(0);  // step s + 2 (unused after the last pair)
     interleave();
+    fetch_words((r + 3) & 3);
     lds_barrier();
     read_b(0, 0);               // step s + 2 (unused after the last pair)
     mfma_half(A1, 4);
