@@ -201,10 +201,13 @@ __device__ __forceinline__ u32x2 decode_pairs(uint32_t w0, uint32_t w1, uint32_t
   u32x2 out;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    // one fp16 add of each word's halves (SDWA selects), value 2p low, 2p + 1 high
-    out[p] = mcg_value2(h[2 * p], h[2 * p + 1]);
-    if constexpr (CB == 2) {
-      const half2_t v = __builtin_bit_cast(half2_t, out[p]);
+    if constexpr (CB == 1) {
+      // one fp16 add of each word's halves (SDWA selects), value 2p low, 2p + 1 high
+      out[p] = mcg_value2(h[2 * p], h[2 * p + 1]);
+    } else {
+      const uint32_t lo = __builtin_amdgcn_perm(h[2 * p + 1], h[2 * p], 0x05040100u);  // lo halves
+      const uint32_t hi = __builtin_amdgcn_perm(h[2 * p + 1], h[2 * p], 0x07060302u);  // hi halves
+      const half2_t v = __builtin_bit_cast(half2_t, lo) + __builtin_bit_cast(half2_t, hi);
       typedef short sv2 __attribute__((ext_vector_type(2)));
       const sv2 q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(sv2{0, 0}, v, 1.0f, false);
       out[p] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_bit_cast(uint32_t, q), 1.0f, false));
@@ -702,19 +705,34 @@ __device__ __forceinline__ void run_piece_f8(const GemmParams &P, u32x4 (*ring)[
   auto decode_to = [&](int cslot, int slot) {
     const uint32_t *w = reinterpret_cast<const uint32_t *>(cw + cslot * 64);
     uint32_t q[8];
+    // the window words of tiles ti + 2, ti + 3 are read while tiles ti, ti + 1 decode
+    u32x4 cur = {w[lw.d0], w[lw.d1], w[NW + lw.d0], w[NW + lw.d1]};
 #pragma unroll
-    for (int ti = 0; ti < 8; ++ti) {
-      const uint32_t bits = lane_bits(w[ti * NW + lw.d0], w[ti * NW + lw.d1], lw.sh);
-      q[ti] = e4m3_pack4(mcg_hash(lane_state<K>(bits, 0)), mcg_hash(lane_state<K>(bits, 1)),
-                         mcg_hash(lane_state<K>(bits, 2)), mcg_hash(lane_state<K>(bits, 3)));
+    for (int ti = 0; ti < 8; ti += 2) {
+      u32x4 nxt = cur;
+      if (ti + 2 < 8)
+        nxt = u32x4{w[(ti + 2) * NW + lw.d0], w[(ti + 2) * NW + lw.d1], w[(ti + 3) * NW + lw.d0], w[(ti + 3) * NW + lw.d1]};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t bits = lane_bits(cur[2 * h], cur[2 * h + 1], lw.sh);
+        q[ti + h] = e4m3_pack4(mcg_hash(lane_state<K>(bits, 0)), mcg_hash(lane_state<K>(bits, 1)),
+                               mcg_hash(lane_state<K>(bits, 2)), mcg_hash(lane_state<K>(bits, 3)));
+      }
+      cur = nxt;
     }
     ring[slot][wave][0][lane] = u32x4{q[0], q[1], q[2], q[3]};
     ring[slot][wave][1][lane] = u32x4{q[4], q[5], q[6], q[7]};
   };
   auto mfma_step = [&](const u32x4 (&a)[4][2], int slot) {
+    // column block nb + 1's operand is read while nb's four MFMAs run
+    u32x4 c0 = ring[slot][0][0][lane], c1 = ring[slot][0][1][lane];
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      const u32x4 b0 = ring[slot][nb][0][lane], b1 = ring[slot][nb][1][lane];
+      const u32x4 b0 = c0, b1 = c1;
+      if (nb + 1 < 8) {
+        c0 = ring[slot][nb + 1][0][lane];
+        c1 = ring[slot][nb + 1][1][lane];
+      }
       const intx8 bv = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
