@@ -10,6 +10,9 @@ bounded sample.
 
 Weights are rotated over enough distinct device copies (> 1 GiB in total) that the 256 MB
 Infinity Cache cannot serve them between steps; inputs are resident in HBM before timing.
+Every timed leg runs at least 50 ms of the same untimed work first (the GPU's clocks take
+~20-30 ms of sustained load to rise after an idle spell), then its W warm-up steps, then
+exactly K timed steps; the line's "clock_ramp" says how much ramp work each leg ran.
 
 Prints ONE JSON line (rank 0, N = 1).  --workload selects the other lines (the fused
 routed-expert MLP, the encoder, the standalone entry points, the microbenchmarks).
@@ -185,8 +188,7 @@ def _per_launch_us(torch, fn, R, reps):
     weight copy), replayed `reps` times between HIP events on the capturing stream's
     successor (the events see the launches' own stream: the replays run on it)."""
     g = _capture(torch, lambda: [fn(i) for i in range(R)])
-    g.replay()
-    torch.cuda.synchronize()
+    _ramp(torch, g.replay, "per_launch", min_ms=RAMP_MS / 2)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -196,15 +198,40 @@ def _per_launch_us(torch, fn, R, reps):
     return e0.elapsed_time(e1) * 1e3 / (reps * R)
 
 
-def _time_steps(torch, step, R, warmup, steps):
+# The GPU's clocks rise over the first ~20-30 ms of sustained load after an idle spell (the
+# dense step measured 55-58 us per step in its first milliseconds and 43-44 us from ~25 ms
+# on).  Every timed leg is therefore preceded by at least RAMP_MS of the same untimed work,
+# before its W warm-up steps, so that the K timed steps measure the sustained rate of a
+# decode loop that keeps the GPU busy, not the clock ramp.
+RAMP_MS = 50.0
+RAMP = {"min_ms": RAMP_MS, "legs": {}}
+
+
+def _ramp(torch, run_once, label, min_ms=RAMP_MS, max_calls=100000):
+    """Calls run_once() (untimed) until at least min_ms of GPU time has passed."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    calls = 0
+    while calls < max_calls:
+        run_once()
+        calls += 1
+        e1.record()
+        e1.synchronize()
+        if e0.elapsed_time(e1) >= min_ms:
+            break
+    RAMP["legs"][label] = {"calls": calls, "ms": round(e0.elapsed_time(e1), 1)}
+
+
+def _time_steps(torch, step, R, warmup, steps, label="steps"):
     """Eager warm-up over the weight copies, then HIP graphs of consecutive steps (R steps
-    per graph, as the layers of a captured decode pass follow one another); exactly `steps`
-    timed.  Returns ms per step."""
+    per graph, as the layers of a captured decode pass follow one another): the clock ramp,
+    `warmup` untimed steps, then exactly `steps` timed.  Returns ms per step."""
     for i in range(R):
         step(i)
     torch.cuda.synchronize()
     stack = LayerStack(torch, step, R)
     stack.prepare(warmup, steps)
+    _ramp(torch, lambda: stack.run(R), label)
     stack.run(warmup)
     torch.cuda.synchronize()
     t_s = torch.cuda.Event(enable_timing=True)
@@ -259,7 +286,7 @@ def run_dense(args, torch, tb, synth):
     def step(i):
         tb.trellis_gemv_list([copies[i % R][n] for n in names], xs, ys, ws=ws)
 
-    ms_step = _time_steps(torch, step, R, args.warmup, args.steps)
+    ms_step = _time_steps(torch, step, R, args.warmup, args.steps, "dense")
     launch_us = _per_launch_us(torch, step, R, max(2, args.steps // R))
 
     def chain(i):  # gate+up (shared x) in one launch, then down
@@ -267,7 +294,7 @@ def run_dense(args, torch, tb, synth):
         tb.trellis_gemv_list([c["gate"], c["up"]], xs[:2], ys[:2], ws=ws)
         tb.trellis_gemv_list([c["down"]], xs[2:], ys[2:], ws=ws)
 
-    ms_chain = _time_steps(torch, chain, R, args.warmup, args.steps)
+    ms_chain = _time_steps(torch, chain, R, args.warmup, args.steps, "dense_chain")
     achieved = code_bytes / (launch_us * 1e-6) / 1e9
     value = code_bytes / (ms_step * 1e-3) / 1e9
     ceiling = decode_ceiling(tb, weights / code_bytes)
@@ -319,7 +346,8 @@ def run_prefill(args, torch, tb, synth, fp8=False):
     fn = tb.trellis_gemm_fp8 if fp8 else tb.trellis_gemm
     x = torch.from_numpy(wl.xs["w"]).cuda()
     y = torch.empty((x.shape[0], lin.out_features), dtype=torch.float16, device="cuda")
-    for _ in range(max(10, args.warmup)):  # also lets the clocks settle under the MFMA load
+    _ramp(torch, lambda: fn(L, x, out=y), "prefill_fp8" if fp8 else "prefill")
+    for _ in range(max(10, args.warmup)):
         fn(L, x, out=y)
     torch.cuda.synchronize()
     n = max(10, args.steps // 2)
@@ -357,7 +385,7 @@ def run_small_batch(args, torch, tb, synth, B):
     def step(i):
         tb.trellis_gemv_list([copies[i % R][n] for n in names], xs, ys, ws=ws)
 
-    ms = _time_steps(torch, step, R, args.warmup, args.steps)
+    ms = _time_steps(torch, step, R, args.warmup, args.steps, f"small_batch_B{B}")
     gbs = code_bytes / (ms * 1e-3) / 1e9
     return {"workload": f"small-batch decode K2 B={B} (qkv 5120x10240, z 5120x6144, out 6144x5120; one "
                         "trellis_gemv_list launch per step; consecutive steps over the weight copies in HIP graphs)",
@@ -407,8 +435,7 @@ def run_moe(args, torch, tb, synth):
     chunk = 16
     n_chunks = max(1, args.steps // chunk)
     graphs = [_capture(torch, lambda c=c: [step(64 + c * chunk + j) for j in range(chunk)]) for c in range(n_chunks)]
-    graphs[0].replay()
-    torch.cuda.synchronize()
+    _ramp(torch, graphs[0].replay, "moe")
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for g in graphs:
@@ -481,8 +508,7 @@ def run_moe_mlp(args, torch, tb, synth, cb=1):
         chunk = 16
         n_chunks = max(1, args.steps // chunk)
         graphs = [_capture(torch, lambda c=c: [fn(64 + c * chunk + j) for j in range(chunk)]) for c in range(n_chunks)]
-        graphs[0].replay()
-        torch.cuda.synchronize()
+        _ramp(torch, graphs[0].replay, f"moe_mlp_{name}_cb{cb}")
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         for g in graphs:
@@ -687,6 +713,7 @@ def main():
             out["copy_probe"] = copy_probe(torch)
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline_dense(wl)
+        out["clock_ramp"] = RAMP
         print(json.dumps(out), flush=True)
     elif args.workload == "small_batch":
         for B in (1, 2, 4, 8):
