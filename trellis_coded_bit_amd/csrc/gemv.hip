@@ -645,10 +645,18 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
         const u32x4 a = *reinterpret_cast<const u32x4 *>(sm.a + (uint32_t)(((k * 8 + 2 * wave + r) * 4 * B) << 2) + a_lane);
         const half8 av = __builtin_bit_cast(half8, a);
         const u32x2 a2 = {__builtin_amdgcn_perm(a[1], a[0], 0x05040100u), __builtin_amdgcn_perm(a[3], a[2], 0x05040100u)};
+        // The tile row's window words are all read before its decode starts (the reads'
+        // LDS latency then overlaps the first tiles' decode instead of every second tile's).
+        uint32_t W0[8], W1[8];
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
           const uint32_t *tw = ub_ + (r * 8 + tt) * NW;
-          const uint32_t bits = lane_bits(tw[lw.d0], tw[lw.d1], lw.sh);
+          W0[tt] = tw[lw.d0];
+          W1[tt] = tw[lw.d1];
+        }
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+          const uint32_t bits = lane_bits(W0[tt], W1[tt], lw.sh);
           u32x4 bw;
           bw[0] = mcg_hash(lane_state<K>(bits, 0));
           bw[1] = mcg_hash(lane_state<K>(bits, 1));
