@@ -421,6 +421,24 @@ __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][
 #pragma unroll
     for (int nb = nb0; nb < nb0 + 4; ++nb) B[nb] = ring[slot][nb][lane];
   };
+  // The second half of a step: activation row block mb's last four MFMAs, then its load for
+  // two steps ahead (the activation loads go out one at a time between MFMAs instead of as
+  // one burst from every wave right after the barrier; 338 -> 336 us per call).
+  auto mfma_half_load = [&](u32x4 (&a)[4], int s_next) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int nb = 4; nb < 8; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a[mb]),
+                                                             __builtin_bit_cast(half8, B[nb]), acc[mb][nb], 0, 0, 0);
+      a[mb] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_off, s_next * 1024 + mb * a_mb, 0);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one activation load
+    }
+  };
   auto mfma_half = [&](const u32x4 (&a)[4], int nb0) {
 #pragma unroll
     for (int nb = nb0; nb < nb0 + 4; ++nb)
@@ -493,8 +511,7 @@ __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][
     fetch_words((r + 2) & 3);  // step s + 2's words (staged above: same wave, in order)
     lds_barrier();
     read_b(1, 0);
-    mfma_half(A0, 4);
-    load_a(A0, s + 2);
+    mfma_half_load(A0, s + 2);
     // (keeps the next step's MFMAs out of this group: hoisted here they would wait on
     // activations loaded only half a step earlier)
     __builtin_amdgcn_sched_barrier(0);
@@ -508,8 +525,7 @@ __device__ __forceinline__ void run_piece(const GemmParams &P, u32x4 (*ring)[8][
     fetch_words((r + 3) & 3);
     lds_barrier();
     read_b(0, 0);               // step s + 2 (unused after the last pair)
-    mfma_half(A1, 4);
-    load_a(A1, s + 3);
+    mfma_half_load(A1, s + 3);
     __builtin_amdgcn_sched_barrier(0);
     // Keeps these B reads in this iteration: with nothing that may write memory after
     // them, the compiler would merge them with the prologue's identical reads into one
