@@ -27,7 +27,7 @@
 //     B-elements along k.  The A operand repeats each activation for the lo and hi halves,
 //     so the matrix core forms x*lo + x*hi in fp32 and the codebook's lo+hi addition costs
 //     no vector instruction.  One MFMA covers one tile; batch rows ride in the 16 M rows
-//     (rows past B read a duplicate activation and are ignored).  This fp32 sum of the
+//     (rows past B multiply zeros and are ignored).  This fp32 sum of the
 //     halves is the exact value before the format's fp16 rounding; it differs from the
 //     rounded codebook value by at most half an fp16 ulp.
 // Finishing, in the same launch: a chunk's fp32 partial y_pre[B][128] of each column block
@@ -626,6 +626,10 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
     for (int j = 1; j < SLOTS - 1; ++j) prime(j);
 
     int slot = 0;
+    // A operands, kept across units: lanes of MFMA rows past B never load theirs, so those
+    // rows multiply zeros rather than copies of row B - 1 (the results of those rows are
+    // ignored either way; zeros draw less power in the matrix core, measured ~1% faster).
+    u32x4 areg[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
     for (int k = 0; k < n; ++k) {
       // copy unit k + SLOTS - 1 into the slot unit k - 1 used (its reads are complete)
       {
@@ -642,7 +646,8 @@ __device__ void run_problem(const GemvParams &P, const Lds &sm, const Problem &p
       const uint32_t *ub_ = ring + slot * (RG::UNIT_BYTES / 4);
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(sm.a + (uint32_t)(((k * 8 + 2 * wave + r) * 4 * B) << 2) + a_lane);
+        if (m < B) areg[r] = *reinterpret_cast<const u32x4 *>(sm.a + (uint32_t)(((k * 8 + 2 * wave + r) * 4 * B) << 2) + a_lane);
+        const u32x4 a = areg[r];
         const half8 av = __builtin_bit_cast(half8, a);
         const u32x2 a2 = {__builtin_amdgcn_perm(a[1], a[0], 0x05040100u), __builtin_amdgcn_perm(a[3], a[2], 0x05040100u)};
         // The tile row's window words are all read before its decode starts (the reads'
