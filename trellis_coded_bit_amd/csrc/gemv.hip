@@ -10,10 +10,8 @@
 // One launch per problem list.  A "unit" is one 128-row input block I times one 128-column
 // output block J of one problem, i.e. 8x8 tiles; units are numbered problem by problem,
 // column block by column block, I fastest.  They are cut into "chunks" of consecutive
-// units: G equal big chunks first, one per workgroup (every one resident at once), then a
-// tail of small chunks.  A workgroup runs its big chunk, then takes small chunks from a
-// queue (one device-scope atomic each) until none is left, so the compute units that start
-// late (the XCDs are dispatched one after another) or run slow take fewer of them.  Inside a workgroup
+// units: G equal chunks, one per workgroup, every workgroup resident at once (so every one
+// streams the same code bytes whatever the shapes or widths).  Inside a workgroup
 // (4 waves) every wave takes two of the unit's eight tile rows:
 //   * loads: the wave's 2 x 8 tiles are 2 x 256K contiguous bytes, copied straight from
 //     global memory into a wave-private LDS ring (global_load_lds, 16 B per lane, fully
@@ -71,20 +69,16 @@ constexpr float kOutScale = 0.125f;  // 2^-7 / 2^-4: the rest of the two 1/sqrt(
 struct GemvParams {
   // (the fields read before a workgroup's first code copy come first)
   int U;                // total units
-  int CH;               // units per big chunk (chunks 0 .. G-1)
-  int CHs;              // units per small chunk (the tail, chunks G ..)
-  int big_units;        // units in the big chunks: min(U, G * CH)
-  int n_chunks;
-  int G;                // workgroups
+  int CH;               // units per chunk (chunk c = workgroup c; the last may be shorter)
+  int G;                // workgroups = chunks
   int kA;               // units per sub-range (A-operand capacity)
   int maxseg;           // column blocks a chunk can touch
   int nI, nJ;           // table mode: the uniform shape in blocks
   int ubase[kMaxList + 1];  // list mode: first unit of each problem (U past the last)
   int qbase[kMaxList + 1];  // list mode: first column block of each problem
   uint32_t *errword;
-  uint32_t *queue;      // [2]: chunks handed out past the first G; workgroups done
   uint32_t *counters;   // [finish groups], zero between calls
-  float *partials;      // [n_chunks][maxseg][B][128]
+  float *partials;      // [G][maxseg][B][128]
   long long partial_bytes;
   GemvLaunch L;
 };
@@ -216,15 +210,9 @@ __device__ __forceinline__ int block_of_unit(const GemvParams &P, int u) {
 struct BlockChunks {
   int lo, hi, seg_lo;
 };
-__device__ __forceinline__ int chunk_start(const GemvParams &P, int c) {
-  return c < P.G ? c * P.CH : P.big_units + (c - P.G) * P.CHs;
-}
-__device__ __forceinline__ int chunk_end(const GemvParams &P, int c) {
-  return c < P.G ? min(P.big_units, (c + 1) * P.CH) : min(P.U, P.big_units + (c + 1 - P.G) * P.CHs);
-}
-__device__ __forceinline__ int chunk_of(const GemvParams &P, int u) {
-  return u < P.big_units ? u / P.CH : P.G + (u - P.big_units) / P.CHs;
-}
+__device__ __forceinline__ int chunk_start(const GemvParams &P, int c) { return c * P.CH; }
+__device__ __forceinline__ int chunk_end(const GemvParams &P, int c) { return min(P.U, (c + 1) * P.CH); }
+__device__ __forceinline__ int chunk_of(const GemvParams &P, int u) { return u / P.CH; }
 template <bool LIST>
 __device__ __forceinline__ BlockChunks block_chunks(const GemvParams &P, int q) {
   const int p = problem_of_block<LIST>(P, q);
@@ -909,10 +897,9 @@ __device__ void finish_weighted(const GemvParams &P, const Lds &sm, int J) {
 
 // End of chunk c: count the chunk in at the finish group of each of its segments; finish
 // the groups whose count this brings to the number of chunks covering them, and reset their
-// counters.  The workgroup's next chunk is taken from the queue in the same round trip and
-// left in *next (LDS).
+// counters.
 template <bool LIST>
-__device__ void arrive_chunk(const GemvParams &P, const Lds &sm, int c, int *next) {
+__device__ void arrive_chunk(const GemvParams &P, const Lds &sm, int c) {
   const int cu0 = chunk_start(P, c), cu1 = chunk_end(P, c);
   const int q0 = block_of_unit<LIST>(P, cu0), q1 = block_of_unit<LIST>(P, cu1 - 1);
   __builtin_amdgcn_s_setprio(3);  // the arrivals and finishes ahead of other workgroups' decode
@@ -920,13 +907,7 @@ __device__ void arrive_chunk(const GemvParams &P, const Lds &sm, int c, int *nex
   // barrier does not wait for global stores), so an arrival publishes complete partials.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  uint32_t *flags = sm.tiles;  // (the code ring is idle between chunks)
-  // the last thread of the workgroup takes the next chunk number (q1 - q0 < kThreads - 1
-  // whenever a chunk meets fewer column blocks than a workgroup has threads; otherwise it
-  // waits for the first round below)
-  uint32_t got = 0;
-  if (threadIdx.x == kThreads - 1 && P.n_chunks > P.G)
-    got = __hip_atomic_fetch_add(P.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t *flags = sm.tiles;  // (the code ring is idle once the chunk is done)
   for (int base = q0; base <= q1; base += kThreads) {
     const int q = base + (int)threadIdx.x;
     if (q <= q1) {
@@ -934,7 +915,6 @@ __device__ void arrive_chunk(const GemvParams &P, const Lds &sm, int c, int *nex
       const uint32_t old = __hip_atomic_fetch_add(P.counters + f, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       flags[threadIdx.x] = old + 1 == (uint32_t)group_arrivals<LIST>(P, f) ? 1u : 0u;
     }
-    if (base == q0 && threadIdx.x == kThreads - 1) *next = P.n_chunks > P.G ? (int)got + P.G : P.n_chunks;
     __syncthreads();
     const int cnt = min(kThreads, q1 - base + 1);
     // The other chunks' partials are read after their arrivals were seen, with device-scope
@@ -978,14 +958,14 @@ __device__ void arrive_chunk(const GemvParams &P, const Lds &sm, int c, int *nex
 
 // The units [cu0, cu1) of one chunk, problem by problem.
 template <bool LIST, int KS, int CBS>
-__device__ __forceinline__ void run_chunk(const GemvParams &P, const Lds &sm, int c, bool fresh) {
+__device__ __forceinline__ void run_chunk(const GemvParams &P, const Lds &sm, int c) {
   const int cu0 = chunk_start(P, c), cu1 = chunk_end(P, c);
   const int q0 = block_of_unit<LIST>(P, cu0);
   for (int u = cu0; u < cu1;) {
     const int p = problem_of_unit<LIST>(P, u);
     const int ue = min(cu1, units_base<LIST>(P, p + 1));
     const Problem pr = get_problem<LIST>(P, p);
-    const bool f = fresh && u == cu0;
+    const bool f = u == cu0;  // (the workgroup's first part: nothing earlier to wait for)
     if constexpr (KS != 0) {
       run_problem<KS, CBS, LIST>(P, sm, pr, p, u, ue, c, q0, f);
     } else {
@@ -1008,28 +988,14 @@ __device__ __forceinline__ void run_chunk(const GemvParams &P, const Lds &sm, in
 template <bool LIST, int KS, int CBS>
 __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(GemvParams P) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
-  __shared__ int next_chunk;
   const Lds sm = lds_carve(lds_raw, P.L.B, P.kA);
-  int c = blockIdx.x;  // (the launch keeps G <= n_chunks)
-  for (bool fresh = true;; fresh = false) {
-    // Top issue priority for the chunk's set-up: its loads go out while other workgroups on
-    // the CU decode (and a workgroup dispatched after its CU's others are already decoding
-    // would otherwise run its prologue at the lowest priority, behind them).
-    __builtin_amdgcn_s_setprio(3);
-    run_chunk<LIST, KS, CBS>(P, sm, c, fresh);
-    arrive_chunk<LIST>(P, sm, c, &next_chunk);
-    c = next_chunk;
-    if (c >= P.n_chunks) break;
-  }
-  // The last workgroup to leave resets the queue for the next call (every workgroup has taken
-  // its last chunk number before it counts itself out).
-  if (threadIdx.x == 0 && P.n_chunks > P.G) {
-    const uint32_t done = __hip_atomic_fetch_add(P.queue + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == (uint32_t)P.G - 1) {
-      __hip_atomic_store(P.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(P.queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  const int c = blockIdx.x;  // (chunk c; the launch has exactly G = chunks workgroups)
+  // Top issue priority for the chunk's set-up: its loads go out while other workgroups on
+  // the CU decode (and a workgroup dispatched after its CU's others are already decoding
+  // would otherwise run its prologue at the lowest priority, behind them).
+  __builtin_amdgcn_s_setprio(3);
+  run_chunk<LIST, KS, CBS>(P, sm, c);
+  arrive_chunk<LIST>(P, sm, c);
 }
 
 // An empty weighted sum (no routed experts): y = 0.
@@ -1067,20 +1033,12 @@ int device_cus_and_occupancy(int B, int *cus_out) {
 
 struct Geometry {
   bool ok = false;
-  int U = 0, G = 0, CH = 0, CHs = 0, big_units = 0, n_chunks = 0, maxseg = 0, kA = 0, nq = 0, nf = 0;
+  int U = 0, G = 0, CH = 0, maxseg = 0, kA = 0, nq = 0, nf = 0;
   int ubase[kMaxList + 1] = {}, qbase[kMaxList + 1] = {};
   size_t partial_bytes = 0, bytes = 0;
 };
 
-// The share of the units left to the small chunks, and their size.  Measured on the dense
-// MLP step, every tail share tried (5-30%, chunks of 1-4 units) was slower than none: each
-// small chunk pays the set-up latency of its rotation and first code copies (a few
-// microseconds) at the end of the launch, where few workgroups remain to cover it.  The
-// default is therefore one equal static share per workgroup; the tail stays available.
-constexpr double kTailShare = 0.0;
 constexpr int kMinChunkAt4 = 13;
-constexpr int kSmallChunk = 2;
-constexpr int kMaxChunk = 32;
 
 Geometry geometry(const GemvLaunch &a) {
   Geometry gm;
@@ -1130,44 +1088,27 @@ Geometry geometry(const GemvLaunch &a) {
   // the dense MLP step, 16 units, is faster at four: 45.4 against 48.0 us).
   if (occ >= 4 && U < (long long)kMinChunkAt4 * cus * occ) occ = 3;
   long long G = (long long)cus * occ;
-  // Debug/test overrides of the workgroup count and the chunk size (they exercise chunks
-  // that span column blocks and problems, and many chunks per workgroup).
+  // Debug/test override of the workgroup count (it exercises chunks that span column blocks
+  // and problems).
   if (const char *env = getenv("TRELLIS_GEMV_WGS")) {
     const long long v = atoll(env);
     if (v > 0) G = v;
   }
   if (G > U) G = U;
   if (G < 1) G = 1;
-  // The big chunks take (1 - tail) of the units in equal shares, the small ones the rest.
-  double tail = kTailShare;
-  if (const char *env = getenv("TRELLIS_GEMV_TAIL")) tail = atof(env);
-  if (tail < 0) tail = 0;
-  if (tail > 1) tail = 1;
-  long long CH = (long long)((double)U * (1.0 - tail) / (double)G);
-  if (tail == 0) CH = (U + G - 1) / G;
-  if (CH < 1) CH = 1;
-  long long CHs = kSmallChunk;
-  if (const char *env = getenv("TRELLIS_GEMV_CHUNK")) {
-    const long long v = atoll(env);
-    if (v > 0) CHs = v;
-  }
-  if (CHs > kMaxChunk) CHs = kMaxChunk;
-  const long long big = U < G * CH ? U : G * CH;
+  // equal chunks, one per workgroup; none may be empty
+  const long long CH = (U + G - 1) / G;
+  G = (U + CH - 1) / CH;
   gm.CH = (int)CH;
-  gm.CHs = (int)CHs;
-  gm.big_units = (int)big;
-  // every workgroup owns one big chunk, so none may be empty
-  G = (big + CH - 1) / CH;
   gm.G = (int)G;
-  gm.n_chunks = (int)(G + (U - big + CHs - 1) / CHs);
   // a chunk of n units meets at most (n - 1) / nI_min + 2 column blocks
-  const long long chmax = CH > CHs ? CH : CHs;
+  const long long chmax = CH;
   const long long maxseg = (chmax - 1) / nI_min + 2;
   gm.maxseg = (int)(maxseg < nq ? maxseg : nq);
   long long kA_max = kABudget / (512 * B);
   if (kA_max > (long long)kWaves * kMaxTasks / B) kA_max = (long long)kWaves * kMaxTasks / B;
   gm.kA = (int)(chmax < kA_max ? chmax : kA_max);
-  gm.partial_bytes = (size_t)gm.n_chunks * gm.maxseg * B * 128 * sizeof(float);
+  gm.partial_bytes = (size_t)gm.G * gm.maxseg * B * 128 * sizeof(float);
   if (gm.partial_bytes >= (1ULL << 31)) return gm;  // 32-bit buffer offsets
   gm.bytes = kWsReserved + gm.partial_bytes;
   gm.ok = true;
@@ -1188,15 +1129,11 @@ hipError_t launch_list(const GemvLaunch &a, char *ws, float *partials, size_t pa
   P.L = a;
   if (P.L.group < 1) P.L.group = 1;
   P.errword = reinterpret_cast<uint32_t *>(ws);
-  P.queue = reinterpret_cast<uint32_t *>(ws + kWsQueueOffset);
   P.counters = reinterpret_cast<uint32_t *>(ws + kWsHeaderBytes);
   P.partials = partials;
   P.partial_bytes = (long long)gm.partial_bytes;
   P.U = gm.U;
   P.CH = gm.CH;
-  P.CHs = gm.CHs;
-  P.big_units = gm.big_units;
-  P.n_chunks = gm.n_chunks;
   P.G = gm.G;
   P.maxseg = gm.maxseg;
   P.kA = gm.kA;

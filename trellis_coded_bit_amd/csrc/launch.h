@@ -25,14 +25,12 @@ hipError_t launch_had128(const void *x, int x_is_fp32, int rows, int n, const ui
 // Every workspace starts with the same reserved region, so that one zero-filled buffer can
 // serve every entry point in any order:
 //   [0, 256)                 header; word 0 is the error word (sticky: kernels only OR bits
-//                            into it, the caller clears it); words 16-17 the small-batch
-//                            products' chunk queue (zero between calls)
+//                            into it, the caller clears it); the other words are unused
 //   [256, 256 + 64 KiB)      the small-batch products' column-block counters: zero between
 //                            calls (each call's finishing workgroups reset the ones it used);
 //                            no other entry point writes them
 //   [kWsReserved, ...)       the entry point's own scratch
 constexpr size_t kWsHeaderBytes = 256;
-constexpr size_t kWsQueueOffset = 64;  // header words 16, 17: the small-batch chunk queue (zero between calls)
 constexpr int kMaxFinishGroups = 16384;
 constexpr size_t kWsCounterBytes = (size_t)kMaxFinishGroups * 4;
 constexpr size_t kWsReserved = kWsHeaderBytes + kWsCounterBytes;
