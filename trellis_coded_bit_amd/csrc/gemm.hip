@@ -739,8 +739,19 @@ __device__ __forceinline__ void run_piece_f8(const GemmParams &P, u32x4 (*ring)[
     ring[slot][wave][0][lane] = u32x4{q[0], q[1], q[2], q[3]};
     ring[slot][wave][1][lane] = u32x4{q[4], q[5], q[6], q[7]};
   };
-  auto mfma_step = [&](const u32x4 (&a)[4][2], int slot) {
-    // column block nb + 1's operand is read while nb's four MFMAs run
+  // One step: its 32 MFMAs on B slot `slot` (column block nb + 1's operand is read while
+  // nb's four MFMAs run) and the decode of the next step's eight tiles (codes in code ring
+  // slot `cslot`, into B slot `dslot`), one tile per column block, issued between the MFMAs
+  // five vector instructions at a time.
+  auto step = [&](const u32x4 (&a)[4][2], int slot, int cslot, int dslot) {
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(cw + cslot * 64);
+    uint32_t wd0[8], wd1[8];
+#pragma unroll
+    for (int ti = 0; ti < 8; ++ti) {
+      wd0[ti] = w[ti * NW + lw.d0];
+      wd1[ti] = w[ti * NW + lw.d1];
+    }
+    uint32_t q[8];
     u32x4 c0 = ring[slot][0][0][lane], c1 = ring[slot][0][1][lane];
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
@@ -756,6 +767,21 @@ __device__ __forceinline__ void run_piece_f8(const GemmParams &P, u32x4 (*ring)[
                           (int)a[mb][1][0], (int)a[mb][1][1], (int)a[mb][1][2], (int)a[mb][1][3]};
         acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mb][nb], 0, 0, 0, 0, 0, 0);
       }
+      const uint32_t bits = lane_bits(wd0[nb], wd1[nb], lw.sh);
+      q[nb] = e4m3_pack4(mcg_hash(lane_state<K>(bits, 0)), mcg_hash(lane_state<K>(bits, 1)),
+                         mcg_hash(lane_state<K>(bits, 2)), mcg_hash(lane_state<K>(bits, 3)));
+    }
+    ring[dslot][wave][0][lane] = u32x4{q[0], q[1], q[2], q[3]};
+    ring[dslot][wave][1][lane] = u32x4{q[4], q[5], q[6], q[7]};
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five vector instructions
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
   };
 
@@ -787,15 +813,13 @@ __device__ __forceinline__ void run_piece_f8(const GemmParams &P, u32x4 (*ring)[
     // step st: B slot 0, A0
     stage_c(CR0, (r + 2) & 3);
     load_c(CR0, st + 4);
-    decode_to((r + 1) & 3, 1);  // step st + 1
-    mfma_step(A0, 0);
+    step(A0, 0, (r + 1) & 3, 1);  // MFMAs of step st, decode of step st + 1
     lds_barrier();
     load_a(A0, st + 2);
     if (st + 1 < k1) {  // (uniform) step st + 1: B slot 1, A1
       stage_c(CR1, (r + 3) & 3);
       load_c(CR1, st + 5);
-      decode_to((r + 2) & 3, 0);  // step st + 2
-      mfma_step(A1, 1);
+      step(A1, 1, (r + 2) & 3, 0);  // MFMAs of step st + 1, decode of step st + 2
       lds_barrier();
       load_a(A1, st + 3);
     }
