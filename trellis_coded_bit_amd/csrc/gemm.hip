@@ -718,6 +718,7 @@ __device__ __forceinline__ void run_piece_f8(const GemmParams &P, u32x4 (*ring)[
     c = __builtin_amdgcn_raw_buffer_load_b128(rc, c_off, 0, 0);
   };
   auto stage_c = [&](const u32x4 &c, int slot) { cw[slot * 64 + cc] = c; };  // repeated lanes store equal data
+  // The decode of the piece's first step (before the loop; the loop decodes in `step`).
   auto decode_to = [&](int cslot, int slot) {
     const uint32_t *w = reinterpret_cast<const uint32_t *>(cw + cslot * 64);
     uint32_t q[8];
