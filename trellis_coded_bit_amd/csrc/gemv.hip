@@ -1081,18 +1081,34 @@ Geometry geometry(const GemvLaunch &a) {
   gm.nf = a.table && a.finish == kFinishSwiGLU ? gm.nq / 2
         : a.table && a.finish == kFinishWeighted ? a.out_features / 128 : gm.nq;
   int cus = 0;
-  int occ = device_cus_and_occupancy(B, &cus);
+  const int occ_lds = device_cus_and_occupancy(B, &cus);
+  int occ = occ_lds;
   // Short chunks amortise a workgroup's set-up and finish latency poorly: with fewer than
   // kMinChunkAt4 units each at four workgroups per CU, three per CU are used (measured on
   // the MoE token, whose launches give 6-12 units per workgroup: 65.5 against 70-73 us;
   // the dense MLP step, 16 units, is faster at four: 45.4 against 48.0 us).
   if (occ >= 4 && U < (long long)kMinChunkAt4 * cus * occ) occ = 3;
   long long G = (long long)cus * occ;
+  // units per sub-range: the A-operand region holds kWaves * kMaxTasks (unit, row) rotations
+  long long kA_max = kABudget / (512 * B);
+  if (kA_max > (long long)kWaves * kMaxTasks / B) kA_max = (long long)kWaves * kMaxTasks / B;
   // Debug/test override of the workgroup count (it exercises chunks that span column blocks
   // and problems).
+  bool forced = false;
   if (const char *env = getenv("TRELLIS_GEMV_WGS")) {
     const long long v = atoll(env);
-    if (v > 0) G = v;
+    if (v > 0) {
+      G = v;
+      forced = true;
+    }
+  }
+  // A chunk longer than kA_max units runs in several sub-ranges, each paying a rotation
+  // and about a microsecond at its start.  When the CUs can hold the workgroups that chunks
+  // of kA_max units need, use those (the small-batch step at B = 2, kA_max = 8: 880
+  // workgroups of 8 units, 25.6 us, against 768 of 10 units, 27.8 us).
+  if (!forced && (U + G - 1) / G > kA_max) {
+    const long long Gk = (U + kA_max - 1) / kA_max;
+    if (Gk <= (long long)cus * occ_lds) G = Gk;
   }
   if (G > U) G = U;
   if (G < 1) G = 1;
@@ -1105,8 +1121,6 @@ Geometry geometry(const GemvLaunch &a) {
   const long long chmax = CH;
   const long long maxseg = (chmax - 1) / nI_min + 2;
   gm.maxseg = (int)(maxseg < nq ? maxseg : nq);
-  long long kA_max = kABudget / (512 * B);
-  if (kA_max > (long long)kWaves * kMaxTasks / B) kA_max = (long long)kWaves * kMaxTasks / B;
   gm.kA = (int)(chmax < kA_max ? chmax : kA_max);
   gm.partial_bytes = (size_t)gm.G * gm.maxseg * B * 128 * sizeof(float);
   if (gm.partial_bytes >= (1ULL << 31)) return gm;  // 32-bit buffer offsets
