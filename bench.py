@@ -4,7 +4,8 @@ Default workload: the dense-MLP decode step at batch 1 (gate K2 5120->17408, up 
 5120->17408, down K3 17408->5120, each on its own input), one trellis_gemv_list launch per
 step.  Metric: code bytes (in*out*K/8 summed over the three matrices) per second.  The same
 JSON line carries the single-matrix latency, the small-batch decode at B = 1, 2, 4, 8, the
-MoE decode (8 of 256 experts), fp16 and FP8 prefill, the roofline of the step's kernel
+MoE decode (8 of 256 experts), the fused routed-expert MLP token (MCG and E4M3 codebooks),
+fp16 and FP8 prefill, the roofline of the step's kernel
 against HBM with the measured decode ceiling beside it, and the CPU oracle timed on a
 bounded sample.
 
@@ -14,8 +15,8 @@ Every timed leg runs at least 50 ms of the same untimed work first (the GPU's cl
 ~20-30 ms of sustained load to rise after an idle spell), then its W warm-up steps, then
 exactly K timed steps; the line's "clock_ramp" says how much ramp work each leg ran.
 
-Prints ONE JSON line (rank 0, N = 1).  --workload selects the other lines (the fused
-routed-expert MLP, the encoder, the standalone entry points, the microbenchmarks).
+Prints ONE JSON line (rank 0, N = 1).  --workload selects the other lines (the encoder,
+the standalone entry points, the microbenchmarks) or one of the above alone.
 """
 from __future__ import annotations
 
@@ -683,7 +684,7 @@ def main():
     ap.add_argument("--workload", default="dense", choices=["dense", "small_batch", "moe", "moe_mlp", "prefill", "encode", "kernels", "micro"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="dense: skip the single, small-batch and MoE lines")
+    ap.add_argument("--no-extra", action="store_true", help="dense: skip the single, small-batch, MoE and fused-MLP lines")
     ap.add_argument("--no-unfused", action="store_true", help="moe_mlp: time only the fused call")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
@@ -705,6 +706,8 @@ def main():
             out["single"] = run_single(args, torch, tb, synth)
             out["small_batch"] = [run_small_batch(args, torch, tb, synth, B) for B in (1, 2, 4, 8)]
             out["moe"] = run_moe(args, torch, tb, synth)
+            torch.cuda.empty_cache()
+            out["moe_mlp"] = [run_moe_mlp(args, torch, tb, synth), run_moe_mlp(args, torch, tb, synth, cb=2)]
             torch.cuda.empty_cache()
         if not args.no_prefill:
             out["prefill"] = run_prefill(args, torch, tb, synth)
