@@ -799,13 +799,23 @@ __device__ __forceinline__ void run_piece_f8(const GemmParams &P, u32x4 (*ring)[
   // two steps ahead (past the piece they fetch unused data, bounded by the resources).
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the previous piece's stores are done
   load_c(CR0, k0);
-  load_a(A0, k0);
   load_c(CR1, k0 + 1);
-  load_a(A1, k0 + 1);
   stage_c(CR0, 0);
-  load_c(CR0, k0 + 2);
   stage_c(CR1, 1);
+  // The loads left in flight when the loop starts are issued in the order one iteration
+  // leaves them (codes of step k0 + 2, activations of k0, codes of k0 + 3, activations of
+  // k0 + 1): the compiler counts outstanding loads per position and takes, at the loop
+  // head, the stricter of the entry and the back edge, so any other order makes every
+  // iteration wait for loads issued only just before.
+  __builtin_amdgcn_sched_barrier(0);
+  load_c(CR0, k0 + 2);
+  __builtin_amdgcn_sched_barrier(0);
+  load_a(A0, k0);
+  __builtin_amdgcn_sched_barrier(0);
   load_c(CR1, k0 + 3);
+  __builtin_amdgcn_sched_barrier(0);
+  load_a(A1, k0 + 1);
+  __builtin_amdgcn_sched_barrier(0);
   decode_to(0, 0);
   lds_barrier();
   if (signal >= 0 && threadIdx.x == 0)
@@ -819,11 +829,14 @@ __device__ __forceinline__ void run_piece_f8(const GemmParams &P, u32x4 (*ring)[
     load_a(A0, st + 2);
     if (st + 1 < k1) {  // (uniform) step st + 1: B slot 1, A1
       stage_c(CR1, (r + 3) & 3);
-      load_c(CR1, st + 5);
       step(A1, 1, (r + 2) & 3, 0);  // MFMAs of step st + 1, decode of step st + 2
       lds_barrier();
-      load_a(A1, st + 3);
     }
+    // The second step's loads are issued on both paths (unused after an odd last step), so
+    // the compiler counts the same loads in flight at the loop head whichever path ran, and
+    // waits only for the ones a step uses.
+    load_c(CR1, st + 5);
+    load_a(A1, st + 3);
   }
   lds_barrier();  // the rings' last reads are done before the next piece writes them
 }
