@@ -47,8 +47,19 @@ def oracle_w_hat(key, lin) -> np.ndarray:
     return _W_HAT[key]
 
 
-def oracle_forward_full(key, lin, x, null_scales: bool = False) -> np.ndarray:
-    """The oracle's whole output for this layer and input (its decode cached under key)."""
+def oracle_forward_full(key, lin, x, null_scales: bool = False, act_e4m3: bool = False) -> np.ndarray:
+    """The oracle's whole output for this layer and input (its decode cached under key);
+    act_e4m3 selects the FP8 prefill's per-row E4M3 activations."""
     w = oracle_w_hat(key, lin)
     s_in, s_out = (None, None) if null_scales else (lin.s_in, lin.s_out)
-    return O.forward_decoded(w, lin.rin, lin.rout, s_in, s_out, x)
+    return O.forward_decoded(w, lin.rin, lin.rout, s_in, s_out, x, act_e4m3=act_e4m3)
+
+
+def worst_block_rel_l2(y: np.ndarray, ref: np.ndarray, rows: int = 512, cols: int = 128) -> float:
+    """The largest relative L2 over row bands x column blocks: no part of the output may be
+    off on its own while the whole tensor passes."""
+    worst = 0.0
+    for r0 in range(0, ref.shape[0], rows):
+        for c0 in range(0, ref.shape[1], cols):
+            worst = max(worst, rel_l2(y[r0:r0 + rows, c0:c0 + cols], ref[r0:r0 + rows, c0:c0 + cols]))
+    return worst

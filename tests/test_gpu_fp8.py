@@ -14,7 +14,7 @@ import oracle as O
 from trellis_coded_bit_amd import binding as tb
 from trellis_coded_bit_amd import synth
 
-from gpu_util import REL_L2_TOL, log_case, rel_l2, to_dev
+from gpu_util import REL_L2_TOL, log_case, oracle_forward_full, rel_l2, to_dev, worst_block_rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -79,18 +79,19 @@ def test_gemm_fp8_zero_rows_and_determinism():
 
 
 def test_gemm_fp8_prefill_full_size():
-    """K3 5120 -> 17408, M = 2048 (the prefill shape), sampled output column blocks."""
+    """K3 5120 -> 17408, M = 2048 (the prefill shape): every one of the 2048 x 17408 outputs
+    against the oracle's FP8 prefill, and every 512-row band of every column block."""
+    log_case("gemm fp8 prefill full size")
     lin = _fp8_linear([57], 3, 5120, 17408)
     x = synth.make_x(np.random.SeedSequence(58), 2048, 5120)
     y = _gemm_fp8_np(lin, x)
-    blocks = [0, 77, 135]
-    ref = O.forward_linear(lin, x, col_blocks=blocks, act_e4m3=True)
-    got = np.concatenate([y[:, 128 * J:128 * J + 128] for J in blocks], axis=1)
-    assert rel_l2(got, ref) < REL_L2_TOL
+    ref = oracle_forward_full(("fp8 prefill", 57), lin, x, act_e4m3=True)
+    assert rel_l2(y, ref) < REL_L2_TOL
+    assert worst_block_rel_l2(y, ref) < REL_L2_TOL
     # the FP8 path against the unquantised activations: the E4M3 rounding of xh costs a
     # few percent, as the oracle's own band says
-    exact = O.forward_linear(lin, x[:64], col_blocks=blocks[:1])
-    assert 0.005 < rel_l2(y[:64, :128], exact) < 0.05
+    exact = oracle_forward_full(("fp8 prefill", 57), lin, x[:64])
+    assert 0.005 < rel_l2(y[:64], exact) < 0.05
 
 
 # ------------------------------------------------------------------------------------------
@@ -109,15 +110,19 @@ def test_gemv_e4m3_codebook(K, n_in, n_out, B):
 
 
 def test_gemv_e4m3_codebook_full_size():
-    """up_proj shape K3 5120 -> 17408 with the E4M3 codebook, batch 1, sampled blocks."""
+    """up_proj shape K3 5120 -> 17408 with the E4M3 codebook, batch 1 and 8: the whole
+    output and every column block."""
+    log_case("gemv e4m3 full size")
     lin = _fp8_linear([62], 3, 5120, 17408)
-    x = synth.make_x(np.random.SeedSequence(63), 1, 5120)
-    y = tb.trellis_gemv(tb.TrellisLinear.from_host(lin), to_dev(x))
-    torch.cuda.synchronize()
-    blocks = [0, 70, 135]
-    ref = O.forward_linear(lin, x, col_blocks=blocks)
-    got = np.concatenate([y.cpu().numpy()[:, 128 * J:128 * J + 128] for J in blocks], axis=1)
-    assert rel_l2(got, ref) < REL_L2_TOL
+    L = tb.TrellisLinear.from_host(lin)
+    for B in (1, 8):
+        x = synth.make_x(np.random.SeedSequence([63, B]), B, 5120)
+        y = tb.trellis_gemv(L, to_dev(x))
+        torch.cuda.synchronize()
+        y = y.cpu().numpy()
+        ref = oracle_forward_full(("e4m3 gemv", 62), lin, x)
+        assert rel_l2(y, ref) < REL_L2_TOL, B
+        assert worst_block_rel_l2(y, ref) < REL_L2_TOL, B
 
 
 def test_moe_table_mixing_codebooks():
